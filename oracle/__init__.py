@@ -1,0 +1,234 @@
+"""Plain CPU oracle for source projection of a vocab-sharded output head.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the GPU library (``logit_source_projection_amd``) and imports nothing from
+it; the product path never calls it.
+
+Sources (SemBridge: Compiling Consumer Observations into Cross-Stack
+Communication Plans):
+
+* section 5.2 (Data, Result, and Control Paths): the tail output head
+  materialises the full logits; the full-logit plan slices them by TP lane,
+  transfers the shards and reconstructs the whole tensor with a
+  destination-local AllGather, while a token-only request applies the native
+  (deterministic) sampler to the same tensor and ships int32 IDs;
+* section 5.3 / section 6 (Plan Realization, Evaluation): source projection
+  applies the same argmax before transfer and sends one int32 result per lane;
+* section 3.1 (Boundary Contract): the registered projection operator carries
+  deterministic tie-breaking semantics; section 3.2 (Consumer Observation):
+  a log-probability surface keeps the complete logits plus token IDs;
+* Figure 1 caption: full-logit transfer and source projection deliver the
+  same requested token ID.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+
+* the deterministic sampler is greedy argmax over the raw logits, and ties go
+  to the lowest global vocabulary index;
+* log-probabilities are log-softmax of the raw logits (no temperature, bias or
+  soft-cap); the selected-token log-probability belongs to the argmax token;
+* the argmax decision is taken on the logits rounded to float32 (the GPU
+  path's logit precision; the pages name none); the fp64 decision is returned
+  beside it for reporting;
+* a row is a "near tie" when its fp64 top-2 gap is below 2e-3 * max_v |z|.
+
+Parity pins: every function here is pinned in ``tests/test_oracle_*.py`` by
+exact-rational brute force, closed forms and invariants; none is "parity
+unpinned".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+NEAR_TIE_REL = 2e-3
+
+
+def _load():
+    """Load liboracle.so, building it first only when it does not exist."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_logits.restype = ctypes.c_int
+    lib.oracle_logits.argtypes = [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def max_threads():
+    """Threads the C oracle's parallel loop uses when nthreads is not given."""
+    return _load().oracle_max_threads()
+
+
+def bf16_bits_to_f64(bits):
+    """Exact decode of bfloat16 bit patterns (uint16) to float64.
+
+    A bf16 pattern is the top half of the float32 with the same value, so the
+    decode is a shift into a uint32 followed by a float32 -> float64 widening,
+    both exact.
+    """
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def logits(x_bits, w_bits, rows=None, nthreads=0):
+    """fp64 head logits z = X . W (SemBridge section 5.2: the tail output head
+    materialises the full logits before either result plan).
+
+    x_bits : uint16 [B, H] bf16 bit patterns of the hidden rows
+    w_bits : uint16 [H, V] bf16 bit patterns of the head weight (all k lanes
+             side by side: lane i is columns [off_i, off_{i+1}))
+    rows   : optional list of row indices of X to evaluate (sampled checks)
+    Returns float64 [len(rows) or B, V]; each entry is summed in ascending h.
+    """
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    if x.ndim != 2 or w.ndim != 2 or x.shape[1] != w.shape[0]:
+        raise ValueError("oracle.logits: need x [B,H] and w [H,V]")
+    B, H = x.shape
+    V = w.shape[1]
+    if rows is None:
+        sel = None
+        n = B
+    else:
+        sel = np.ascontiguousarray(rows, dtype=np.int32)
+        if sel.ndim != 1 or (sel.size and (sel.min() < 0 or sel.max() >= B)):
+            raise ValueError("oracle.logits: row index out of range")
+        n = sel.size
+    z = np.empty((n, V), dtype=np.float64)
+    rc = _load().oracle_logits(
+        x.ctypes.data, H, None if sel is None else sel.ctypes.data, n,
+        w.ctypes.data, V, H, V, z.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_logits failed")
+    return z
+
+
+def check_lanes(lane_off, V):
+    """Lanes are contiguous, non-empty vocab ranges covering [0, V)
+    (SemBridge section 5.2: the logits are sliced by TP lane)."""
+    off = [int(o) for o in lane_off]
+    if len(off) < 2 or off[0] != 0 or off[-1] != V:
+        raise ValueError("lane offsets must start at 0 and end at V")
+    if any(b <= a for a, b in zip(off[:-1], off[1:])):
+        raise ValueError("lane offsets must be strictly increasing")
+    return off
+
+
+def lane_pairs(z, lane_off, decide_dtype=np.float32):
+    """Per-lane projection on every row (SemBridge section 6 / Figure 1:
+    argmax runs once per lane, "argmax x k", and each lane yields one result).
+
+    For lane i = [off_i, off_{i+1}) and each row b:
+      M_i[b]  = max over the lane (in decide_dtype, the decision precision)
+      A_i[b]  = smallest global index in the lane attaining M_i[b]
+      mf_i[b] = fp64 max over the lane
+      S_i[b]  = sum over the lane of exp(z - mf_i) in fp64
+    Returns arrays of shape [B, k]: M, A, mf, S.
+    """
+    B, V = z.shape
+    off = check_lanes(lane_off, V)
+    k = len(off) - 1
+    zd = z.astype(decide_dtype)
+    M = np.empty((B, k), dtype=decide_dtype)
+    A = np.empty((B, k), dtype=np.int64)
+    mf = np.empty((B, k), dtype=np.float64)
+    S = np.empty((B, k), dtype=np.float64)
+    for i in range(k):
+        seg_d = zd[:, off[i]:off[i + 1]]
+        seg = z[:, off[i]:off[i + 1]]
+        # np.argmax returns the first occurrence of the maximum: lowest index.
+        a = np.argmax(seg_d, axis=1)
+        A[:, i] = off[i] + a
+        M[:, i] = seg_d[np.arange(B), a]
+        mf[:, i] = seg.max(axis=1)
+        S[:, i] = np.exp(seg - mf[:, i:i + 1]).sum(axis=1)
+    return M, A, mf, S
+
+
+def combine(M, A, mf, S):
+    """Fold the per-lane results in ascending lane order (one int32 result per
+    lane is what source projection ships, SemBridge section 6).
+
+      id  = A_j for the first lane j whose M_j equals max_i M_i
+      lse = m + log(sum_i S_i * exp(mf_i - m)),  m = max_i mf_i
+    Returns (ids int64 [B], lse float64 [B]).
+    """
+    B, k = M.shape
+    best = M.max(axis=1)
+    j = np.argmax(M == best[:, None], axis=1)  # first lane holding the max
+    ids = A[np.arange(B), j]
+    m = mf.max(axis=1)
+    lse = m + np.log((S * np.exp(mf - m[:, None])).sum(axis=1))
+    return ids, lse
+
+
+def full_logit_argmax(z, lane_off, decide_dtype=np.float32):
+    """The full-logit plan inside the oracle (SemBridge section 5.2): the lane
+    shards are reconstructed into the complete [B, V] tensor (the
+    destination-local AllGather) and a plain first-occurrence argmax runs on
+    it."""
+    off = check_lanes(lane_off, z.shape[1])
+    shards = [z[:, off[i]:off[i + 1]] for i in range(len(off) - 1)]
+    full = np.concatenate(shards, axis=1).astype(decide_dtype)
+    return np.argmax(full, axis=1).astype(np.int64)
+
+
+def top2_gap(z):
+    """Largest minus second-largest logit of each row (0 for an exact tie)."""
+    if z.shape[1] < 2:
+        return np.full(z.shape[0], np.inf)
+    top = np.partition(z, -2, axis=1)[:, -2:]
+    return top[:, 1] - top[:, 0]
+
+
+def project(z, lane_off, decide_dtype=np.float32):
+    """Token and log-probability surfaces from fp64 logits z [B, V].
+
+    Returns a dict with
+      ids       int64 [B]  argmax token IDs, lowest index on ties, decided in
+                           decide_dtype (float32: the GPU's logit precision)
+      ids_f64   int64 [B]  the same decision taken in float64 (reporting)
+      lse       float64 [B] logsumexp of each row
+      sel_lp    float64 [B] log-probability of the argmax token
+      lane_max, lane_arg, lane_sumexp   per-lane results, [B, k]
+      gap       float64 [B] fp64 top-2 gap
+      near_tie  bool [B]   gap < 2e-3 * max_v |z|
+    and checks the pages' invariant that the full-logit plan yields the same
+    IDs as per-lane projection (Figure 1 caption; section 6.3).
+    """
+    M, A, mf, S = lane_pairs(z, lane_off, decide_dtype)
+    ids, lse = combine(M, A, mf, S)
+    r0 = full_logit_argmax(z, lane_off, decide_dtype)
+    if not np.array_equal(ids, r0):
+        raise AssertionError("oracle: per-lane projection differs from the full-logit argmax")
+    M64, A64, _, _ = lane_pairs(z, lane_off, np.float64)
+    ids64, _ = combine(M64, A64, mf, S)
+    # The selected token is the argmax token; its logit is the row maximum in
+    # fp64 terms when the fp32 and fp64 decisions agree.
+    sel = z[np.arange(z.shape[0]), ids]
+    gap = top2_gap(z)
+    near = gap < NEAR_TIE_REL * np.abs(z).max(axis=1)
+    return dict(ids=ids, ids_f64=ids64, lse=lse, sel_lp=sel - lse,
+                lane_max=M, lane_arg=A, lane_sumexp=S, lane_maxf=mf,
+                gap=gap, near_tie=near)
+
+
+def logprobs(z, lse):
+    """Complete log-probabilities lp[b, v] = z[b, v] - lse[b] (the
+    log-probability surface keeps the complete logits, SemBridge section 3.2
+    and 3.4)."""
+    return z - np.asarray(lse, dtype=np.float64)[:, None]
