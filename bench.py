@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the source-projection head on one MI355X.
+
+One step = one token-only projection (sb_project_tokens) of the dense decode
+head: B=16 hidden rows, H=5120, V=151936 in k=4 lanes of 37984, inputs already
+resident in HBM.  Prints ONE JSON line with rows/s, the roofline fraction of
+the head GEMM kernel, the oracle's CPU rate on the same input, and (under
+"report") the full-logit plan and the log-probability surface timed on the
+same input, in alternating order.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "projected rows/s at V=151936 H=5120 (B=16); % HBM / MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dense_decode",
+                    choices=["tiny", "dense_decode", "moe_decode", "large_vocab", "prefill"])
+    ap.add_argument("--B", type=int, default=None, help="row count override (large_vocab sweep)")
+    ap.add_argument("--surface", default="tokens",
+                    choices=["tokens", "logprobs", "logprobs_full", "full_logits"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-report", action="store_true",
+                    help="skip the extra surfaces timed for the report")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(d, surface):
+    """Bytes the surface must move: the weight, the hidden rows and the
+    outputs, each once (no workspace partials, no padding rows)."""
+    B, H, V = d["B"], d["H"], d["V"]
+    nbytes = H * V * 2 + B * H * 2 + B * 4
+    if surface in ("logprobs", "logprobs_full"):
+        nbytes += 2 * B * 4                     # lse + selected log-prob
+    if surface == "logprobs_full":
+        nbytes += B * V * 4                     # complete log-probs
+    if surface == "full_logits":
+        nbytes += B * V * 4                     # complete logits
+    return nbytes
+
+
+def flops(d):
+    return 2 * d["B"] * d["H"] * d["V"]
+
+
+def result_cut_percent(bytes_projected, bytes_full):
+    """Result-traffic cut of source projection vs full-logit transfer."""
+    return 100.0 * (1.0 - bytes_projected / bytes_full)
+
+
+class Runner:
+    """Holds device buffers and issues one call of a surface on a stream."""
+
+    def __init__(self, d, stream):
+        import torch
+        from logit_source_projection_amd import sb
+        self.sb = sb
+        self.torch = torch
+        self.stream = stream
+        dev = torch.device("cuda:0")
+        self.x = sb.to_device_bf16(d["x"], dev)
+        self.w = sb.to_device_bf16(d["w"], dev)
+        self.head = sb.Head(self.x, self.w, d["lane_off"])
+        B, V = d["B"], d["V"]
+        self.ids = torch.empty(B, dtype=torch.int32, device=dev)
+        self.ids_r0 = torch.empty(B, dtype=torch.int32, device=dev)
+        self.lse = torch.empty(B, dtype=torch.float32, device=dev)
+        self.sel = torch.empty(B, dtype=torch.float32, device=dev)
+        self._lp = None
+        self._logits = None
+        self.dev = dev
+        self.B, self.V = B, V
+        self.ws = {}
+        for s in (sb.SB_SURF_TOKENS, sb.SB_SURF_LOGPROBS, sb.SB_SURF_LOGPROBS_FULL,
+                  sb.SB_SURF_FULL_LOGITS):
+            n = sb.sb_workspace_bytes(self.head, s)
+            self.ws[s] = torch.zeros(max(n, 16), dtype=torch.uint8, device=dev)
+
+    @property
+    def lp(self):
+        if self._lp is None:
+            self._lp = self.torch.empty(self.B, self.V, dtype=self.torch.float32, device=self.dev)
+        return self._lp
+
+    @property
+    def logits(self):
+        if self._logits is None:
+            self._logits = self.torch.empty(self.B, self.V, dtype=self.torch.float32,
+                                            device=self.dev)
+        return self._logits
+
+    def call(self, surface):
+        sb, st = self.sb, self.stream
+        if surface == "tokens":
+            sb.sb_project_tokens(self.head, self.ids, ws=self.ws[sb.SB_SURF_TOKENS], stream=st)
+        elif surface == "logprobs":
+            sb.sb_project_logprobs(self.head, self.ids, self.lse, self.sel,
+                                   ws=self.ws[sb.SB_SURF_LOGPROBS], stream=st)
+        elif surface == "logprobs_full":
+            sb.sb_project_logprobs(self.head, self.ids, self.lse, self.sel, self.lp,
+                                   ws=self.ws[sb.SB_SURF_LOGPROBS_FULL], stream=st)
+        elif surface == "full_logits":
+            sb.sb_full_logits(self.head, self.logits, self.ids_r0,
+                              ws=self.ws[sb.SB_SURF_FULL_LOGITS], stream=st)
+        else:
+            raise ValueError(surface)
+
+    def time_calls(self, surface, steps):
+        """Average ms per call over `steps` back-to-back calls, with HIP
+        events recorded on the stream the kernels run on."""
+        torch = self.torch
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(self.stream)
+        for _ in range(steps):
+            self.call(surface)
+        stop.record(self.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
+
+
+def cpu_baseline(d):
+    """The oracle as it stands, timed on this host's cores, on the whole
+    benchmark input (every row over the whole vocabulary)."""
+    import oracle
+    t0 = time.perf_counter()
+    z = oracle.logits(d["x"], d["w"])
+    r = oracle.project(z, d["lane_off"])
+    dt = time.perf_counter() - t0
+    return dict(value=d["B"] / dt, unit="rows/s", cores=oracle.max_threads(), kind="oracle",
+                sample=f"all {d['B']} rows x {d['V']} columns of the benchmark input, one pass "
+                       f"(fp64 logits + per-lane projection + logsumexp), {dt:.2f} s"), r
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this head runs on a single MI355X and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from logit_source_projection_amd import inputs
+
+    t0 = time.perf_counter()
+    d = inputs.make_workload(args.workload, B=args.B)
+    gen_s = time.perf_counter() - t0
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        run = Runner(d, stream)
+    torch.cuda.synchronize()
+
+    # warmup, then exactly `steps` timed steps
+    for _ in range(args.warmup):
+        run.call(args.surface)
+    torch.cuda.synchronize()
+    ms = run.time_calls(args.surface, args.steps)
+    torch.cuda.synchronize()
+
+    B = d["B"]
+    rows_s = B / (ms * 1e-3)
+    nbytes = algorithmic_bytes(d, args.surface)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="head GEMM + fused epilogue (whole call)",
+                    algorithmic_bytes=nbytes)
+    if args.workload == "prefill":
+        tf = flops(d) / (ms * 1e-3) / 1e12
+        roofline = dict(bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=None,
+                        kernel="head GEMM (whole call)", algorithmic_flops=flops(d))
+
+    report = {}
+    if not args.no_report:
+        # token-only vs full-logit plan, alternating AB/BA, same input
+        order = []
+        t_p0, t_r0 = [], []
+        n_pair = max(1, min(10, args.steps // 5))
+        for i in range(2 * n_pair):
+            first = "tokens" if i % 2 == 0 else "full_logits"
+            second = "full_logits" if first == "tokens" else "tokens"
+            for s in (first, second):
+                m = run.time_calls(s, 5)
+                (t_p0 if s == "tokens" else t_r0).append(m)
+            order.append(first[0].upper())
+        torch.cuda.synchronize()
+        same = bool(torch.equal(run.ids, run.ids_r0))
+        report["p0_vs_r0"] = dict(
+            order="".join(order), ms_tokens=round(float(np.median(t_p0)), 4),
+            ms_full_logits=round(float(np.median(t_r0)), 4),
+            ids_identical=same,
+            bytes_out_tokens=4 * B, bytes_out_full_logits=4 * B * d["V"],
+            result_cut_percent=result_cut_percent(4 * B, 4 * B * d["V"]))
+        ms_lp = run.time_calls("logprobs", 10)
+        report["logprobs_ms"] = round(ms_lp, 4)
+        report["tokens_per_s"] = rows_s
+        report["input_sha256"] = dict(
+            x=hashlib.sha256(d["x"].tobytes()).hexdigest()[:16],
+            w=hashlib.sha256(d["w"].tobytes()).hexdigest()[:16])
+        report["input_gen_s"] = round(gen_s, 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu, r = cpu_baseline(d)
+        if not args.no_report:
+            ok = ~r["near_tie"]
+            got = run.ids.cpu().numpy() if args.surface != "full_logits" else run.ids_r0.cpu().numpy()
+            report["ids_match_oracle"] = bool(np.array_equal(got[ok], r["ids"][ok]))
+            report["near_tie_rows"] = [int(i) for i in np.nonzero(r["near_tie"])[0]]
+
+    line = {
+        "metric": METRIC,
+        "value": rows_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": d["H"], "V": d["V"], "k": d["k"],
+                   "surface": args.surface},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "report": report,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

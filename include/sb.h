@@ -1,0 +1,170 @@
+/*
+ * sb.h -- C ABI of libsb: source projection of a vocab-sharded output head
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The head computes logits z = X . W for hidden rows X [B, H] (bf16) and a
+ * head weight W [H, V] (bf16) whose vocabulary is split into k contiguous
+ * lanes, lane i holding vocab columns [off_i, off_{i+1}).  Three result
+ * surfaces are offered, following the SemBridge paper ("SemBridge: Compiling
+ * Consumer Observations into Cross-Stack Communication Plans"):
+ *
+ *  - token-only (sb_project_tokens): section 2.3 and section 5.2 -- a
+ *    deterministic token request applies the sampler (argmax) at the source
+ *    and ships int32 token IDs; section 6 / Figure 1 -- one result per lane
+ *    ("argmax x k"), and all plans deliver the same token ID;
+ *  - log-probability (sb_project_logprobs): section 3.2 / 3.4 -- the surface
+ *    keeps the complete logits plus token IDs; here the logsumexp per row, the
+ *    selected-token log-probability and, on request, the complete fp32
+ *    log-probabilities;
+ *  - full-logit plan (sb_full_logits): section 5.2 / section 6 -- the logits
+ *    are sliced by lane, the shards reconstructed into the complete tensor
+ *    (the destination-local AllGather, here a device-local copy), then argmax.
+ *
+ * Semantics common to every call
+ *  - Token IDs are int32 GLOBAL vocabulary indices.  The registered projection
+ *    is greedy argmax over the fp32 logits; among equal maxima the LOWEST
+ *    global index wins (section 3.1: a projection operator declares
+ *    deterministic tie-breaking).
+ *  - Logits are fp32 sums of exact bf16 x bf16 products.  The order in which
+ *    each logit is accumulated depends only on (B, H), never on the surface,
+ *    the lane split or the column position, so the three calls return
+ *    bit-identical logits and IDs for the same inputs.
+ *  - Inputs must be finite with |logit| < FLT_MAX; behaviour on NaN/Inf input
+ *    is unspecified.
+ *
+ * Ownership and threading
+ *  - The caller allocates every device buffer.  The library allocates no
+ *    device memory, keeps no state between calls and is thread-safe.
+ *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *    the default stream).  Inputs are read-only.  The workspace is scratch
+ *    owned by the call until its work completes on the stream; calls that
+ *    share one workspace must be ordered on one stream.
+ *
+ * Errors
+ *  - Validation is synchronous: on any error status nothing is enqueued and
+ *    no output is touched (missing facts select no silent fallback; section
+ *    3.4's rule that an unavailable fact selects the materialising plan is
+ *    left to the caller, who may call sb_full_logits).
+ *  - SB_ERR_HIP reports a failed kernel launch (hipGetLastError); work may
+ *    then be partially enqueued.
+ */
+#ifndef SB_H
+#define SB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sb_status {
+    SB_OK = 0,
+    SB_ERR_NULL = -1,        /* a required pointer is NULL                     */
+    SB_ERR_SHAPE = -2,       /* B < 0, H < 0, V < 1, or a leading dim too small */
+    SB_ERR_LANES = -3,       /* k < 1, k > SB_MAX_LANES, or lane offsets not
+                                strictly increasing from 0 to V               */
+    SB_ERR_ALIGN = -4,       /* x, w[i], an fp32 output or the workspace not
+                                16-byte aligned; ldx, ldw not multiples of 8;
+                                a logits / log-probs leading dim not a
+                                multiple of 4                                  */
+    SB_ERR_WORKSPACE = -5,   /* workspace smaller than sb_workspace_bytes()   */
+    SB_ERR_UNSUPPORTED = -6, /* B > 65535, or 40 shard rows or 64 rows of x
+                                span 4 GiB or more                            */
+    SB_ERR_HIP = -7          /* a HIP launch failed                            */
+} sb_status;
+
+#define SB_MAX_LANES 64
+
+/* Result surfaces, used to size the workspace. */
+typedef enum sb_surface {
+    SB_SURF_TOKENS = 0,         /* sb_project_tokens                          */
+    SB_SURF_LOGPROBS = 1,       /* sb_project_logprobs, logprobs == NULL      */
+    SB_SURF_LOGPROBS_FULL = 2,  /* sb_project_logprobs, logprobs != NULL      */
+    SB_SURF_FULL_LOGITS = 3     /* sb_full_logits (includes the lane shards)  */
+} sb_surface;
+
+/*
+ * The head.  All shapes in elements.
+ *   B        rows (decode batch / prefill tokens); B == 0 is a valid no-op
+ *   H        hidden size (K of the product); H == 0 gives all-zero logits
+ *   V        vocabulary size, >= 1
+ *   k        number of vocab lanes, 1..SB_MAX_LANES
+ *   lane_off HOST array of k+1 int32: 0 = off_0 < off_1 < ... < off_k = V
+ *   x        DEVICE pointer, bf16 [B][ldx] row-major, 16-byte aligned
+ *   ldx      row stride of x, >= H, multiple of 8
+ *   w        HOST array of k DEVICE pointers; w[i] is lane i's shard, bf16
+ *            [H][ldw] row-major, column j of the shard = vocab column
+ *            off_i + j; 16-byte aligned.  A single [H][V] allocation is
+ *            passed as w[i] = base + off_i with ldw = V (then every off_i
+ *            must be a multiple of 8).
+ *   ldw      row stride of every shard, >= max_i (off_{i+1} - off_i),
+ *            multiple of 8
+ */
+typedef struct sb_head_desc {
+    int32_t B, H, V, k;
+    const int32_t *lane_off;
+    const void *x;
+    int64_t ldx;
+    const void *const *w;
+    int64_t ldw;
+} sb_head_desc;
+
+/*
+ * Bytes of device workspace a call on `desc` with the given surface needs
+ * (0 if none).  Returns 0 and sets *status (if not NULL) to an error code when
+ * the descriptor is invalid.  Host-only; enqueues nothing.
+ */
+size_t sb_workspace_bytes(const sb_head_desc *desc, int surface, sb_status *status);
+
+/*
+ * Token-only surface (source projection, SemBridge section 5.2 / section 6):
+ * ids[b] = lowest global index of max_v z[b][v].  Each lane reduces to one
+ * (max, lowest-index) result per row inside the GEMM epilogue; the per-lane
+ * results are combined in ascending lane order.  The full logits are never
+ * written to memory.
+ *   ids  DEVICE int32 [B]
+ *   ws   DEVICE workspace of >= sb_workspace_bytes(desc, SB_SURF_TOKENS)
+ *        bytes, 16-byte aligned
+ */
+sb_status sb_project_tokens(const sb_head_desc *desc, int32_t *ids,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Log-probability surface (SemBridge section 3.2 / 3.4: complete logits plus
+ * token IDs), computed with an online per-lane logsumexp:
+ *   ids[b]         as sb_project_tokens (bit-identical)
+ *   lse[b]         = log sum_v exp(z[b][v])                       (fp32)
+ *   sel_lp[b]      = z[b][ids[b]] - lse[b]   (optional, may be NULL)
+ *   logprobs[b][v] = z[b][v] - lse[b]        (optional, may be NULL; fp32
+ *                    [B][ldlp], ldlp >= V and a multiple of 4, 16-byte
+ *                    aligned)
+ *   ws  >= sb_workspace_bytes(desc, logprobs ? SB_SURF_LOGPROBS_FULL
+ *                                            : SB_SURF_LOGPROBS)
+ */
+sb_status sb_project_logprobs(const sb_head_desc *desc, int32_t *ids,
+                              float *lse, float *sel_lp, float *logprobs,
+                              int64_t ldlp, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/*
+ * Full-logit plan (SemBridge section 5.2 / section 6, the layout-directed
+ * baseline): every lane writes its fp32 logit shard [B][V_i] into the
+ * workspace, the shards are reconstructed into logits [B][ldl] (the
+ * destination-local AllGather, a device-local copy here), then, if ids is not
+ * NULL, a row argmax (lowest index on ties) yields the token IDs.
+ *   logits DEVICE fp32 [B][ldl], ldl >= V and a multiple of 4, 16-byte aligned
+ *   ids    DEVICE int32 [B] or NULL
+ *   ws     >= sb_workspace_bytes(desc, SB_SURF_FULL_LOGITS)
+ */
+sb_status sb_full_logits(const sb_head_desc *desc, float *logits, int64_t ldl,
+                         int32_t *ids, void *ws, size_t ws_bytes, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *sb_status_string(sb_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SB_H */

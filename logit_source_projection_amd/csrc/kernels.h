@@ -1,0 +1,71 @@
+// Internal launch interface of libsb's HIP kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sbk {
+
+constexpr int kMaxLanes = 64;
+constexpr int kTileN = 128;     // vocab columns per workgroup tile
+constexpr int kStepK = 32;      // hidden rows per MFMA step (16x16x32 bf16)
+constexpr int kWaves = 4;       // waves per workgroup; K steps interleaved over them
+constexpr int kRowBlock = 16;   // rows per MFMA row block
+constexpr int kMaxMB = 4;       // row blocks per workgroup
+constexpr int kArgmaxChunk = 8192;  // columns per workgroup in the full-logit argmax
+
+// Epilogue variants of the head GEMM.
+enum Epilogue : int {
+    kEpiPair = 0,        // (max, lowest index) per (row, tile)
+    kEpiPairLse = 1,     // + (tile max, sum exp(y - tile max)) per (row, tile)
+    kEpiPairLseOut = 2,  // + fp32 logits written at their global column
+    kEpiShard = 3        // fp32 logits written to per-lane shards only
+};
+
+// Per-lane tables, passed by value as a kernel argument.
+struct LaneTable {
+    const uint16_t *w[kMaxLanes];  // lane i's shard base (bf16 bits)
+    float *shard[kMaxLanes];       // lane i's fp32 shard (kEpiShard)
+    int32_t off[kMaxLanes + 1];    // vocab offsets
+    int32_t tile0[kMaxLanes + 1];  // first tile of lane i (prefix sums)
+    int32_t shard_ld[kMaxLanes];   // row stride of lane i's shard
+    int32_t k;
+};
+
+struct HeadArgs {
+    LaneTable lanes;
+    const uint16_t *x;   // bf16 [B][ldx]
+    int64_t ldx;
+    int64_t ldw;
+    int32_t B, H, V;
+    int32_t T;           // total tiles (row stride of the pair workspaces)
+    int2 *pair;          // [B][T] {float bits of max, global index}
+    float2 *mse;         // [B][T] {tile max, sum exp(y - tile max)}
+    float *out;          // [B][ldo] fp32 logits at global columns (kEpiPairLseOut)
+    int64_t ldo;
+};
+
+// Launch the head GEMM with the given epilogue; MB row blocks per workgroup.
+hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s);
+
+// Fold the (row, tile) workspaces into ids / lse / sel_lp (any may be NULL
+// except ids).  One workgroup per row; tiles folded lane by lane in ascending
+// order, lanes folded in ascending order.
+hipError_t launch_combine(const int2 *pair, const float2 *mse, const LaneTable &lanes,
+                          int32_t B, int32_t T, int32_t *ids, float *lse,
+                          float *sel_lp, hipStream_t s);
+
+// lp[b][v] -= lse[b] over [B][V] (row stride ld).
+hipError_t launch_normalize(float *lp, int64_t ld, const float *lse, int32_t B,
+                            int32_t V, hipStream_t s);
+
+// Reconstruct the complete [B][ldl] logits from the per-lane shards.
+hipError_t launch_reconstruct(const LaneTable &lanes, int32_t B, float *logits,
+                              int64_t ldl, hipStream_t s);
+
+// Row argmax (lowest index on ties) of logits [B][ldl] over V columns; needs a
+// workspace of B * ceil(V / kArgmaxChunk) int2.
+hipError_t launch_row_argmax(const float *logits, int64_t ldl, int32_t B, int32_t V,
+                             int2 *partial, int32_t *ids, hipStream_t s);
+
+}  // namespace sbk

@@ -1,0 +1,574 @@
+// HIP kernels of libsb for CDNA4 (gfx950).
+//
+// Head GEMM z = X . W over k vocab lanes, with fused epilogues that reduce
+// each (row, 128-column tile) to a (max, lowest global index) pair and an
+// online (max, sum-exp) pair, or write the fp32 logits.  The SemBridge paper
+// (section 5.2, section 6, Figure 1) ships one argmax result per lane instead
+// of the lane's logits; here every lane is reduced inside the GEMM epilogue
+// and the per-tile results are folded afterwards (combine kernel).
+//
+// Mainloop design (decode shapes are HBM-bound: every weight byte is used by
+// B <= 64 rows only):
+//   * one workgroup = 4 waves = one 128-column tile of one lane, rows
+//     [m0, m0 + 16*MB);
+//   * W is row-major along the vocabulary (column-contiguous), while the
+//     16x16x32 bf16 MFMA wants 8 consecutive K values per lane.  Each lane
+//     loads 8 rows x 8 columns (eight 16-byte loads, 256-byte contiguous
+//     segments per 16 lanes) and transposes them in registers with v_perm;
+//     MFMA number c of a step then covers the strided column set
+//     {c0 + 8n + c : n = 0..15}, so after the eight MFMAs a lane holds eight
+//     consecutive columns of four rows;
+//   * K steps of 32 rows are interleaved over the 4 waves (wave w takes steps
+//     w, w+4, ...); every wave keeps its own fp32 accumulators and the four
+//     partial tiles are added in wave order 0+1+2+3 through LDS.  Each logit
+//     is therefore accumulated in an order fixed by H alone, independent of
+//     the lane split, the column position and the epilogue;
+//   * buffer loads with per-step rebased resources: rows beyond H and
+//     columns beyond the lane's end read as zero without faulting.
+#include "kernels.h"
+
+#include <float.h>
+#include <limits.h>
+
+namespace sbk {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = kWaves * 64;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+                                             (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// (value, index) order: larger value first, then lower index.
+__device__ __forceinline__ bool better(float v1, int i1, float v2, int i2)
+{
+    return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// Online logsumexp merge of (m2, s2) into (m1, s1); -inf marks "empty".
+__device__ __forceinline__ void lse_merge(float &m1, float &s1, float m2, float s2)
+{
+    if (m2 == -INFINITY)
+        return;
+    if (m1 == -INFINITY) {
+        m1 = m2;
+        s1 = s2;
+        return;
+    }
+    if (m2 > m1) {
+        s1 = s1 * __expf(m1 - m2) + s2;
+        m1 = m2;
+    } else {
+        s1 = s1 + s2 * __expf(m2 - m1);
+    }
+}
+
+__device__ __forceinline__ int find_lane(const LaneTable &t, int tile)
+{
+    int lane = 0;
+    while (lane + 1 < t.k && t.tile0[lane + 1] <= tile)
+        ++lane;
+    return lane;
+}
+
+template <int MB>
+struct Frags {
+    u32x4 w[8];
+    u32x4 x[MB];
+};
+
+template <int MB>
+__device__ __forceinline__ void load_step(Frags<MB> &f, const uint16_t *wbase, int64_t wbytes,
+                                          const uint16_t *xbase, int64_t xbytes, int k0,
+                                          int64_t ldw, const uint32_t (&wvo)[8],
+                                          const uint32_t (&xvo)[MB])
+{
+    // Resources rebased to this step's first hidden row: offsets stay small.
+    const int64_t wshift = (int64_t)k0 * ldw;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + wshift, wbytes - wshift * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + k0, xbytes - (int64_t)k0 * 2);
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        f.w[r] = load16(rw, wvo[r]);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        f.x[mb] = load16(rx, xvo[mb]);
+}
+
+template <int MB>
+__device__ __forceinline__ void compute_step(Frags<MB> &f, f32x4 (&acc)[MB][8], int k0, int H,
+                                             int g)
+{
+    if (k0 + kStepK > H) {
+        // K tail: hidden positions >= H must contribute exactly zero even if
+        // the memory past H in a row holds non-finite bits.
+        const int h0 = k0 + 8 * g;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t v = f.x[mb][d];
+                if (h0 + 2 * d >= H)
+                    v &= 0xFFFF0000u;
+                if (h0 + 2 * d + 1 >= H)
+                    v &= 0x0000FFFFu;
+                f.x[mb][d] = v;
+            }
+        }
+    }
+    bf16x8 xa[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        xa[mb] = __builtin_bit_cast(bf16x8, f.x[mb]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        // Column c of the lane's 8x8 block: hidden rows 2q (low half) and
+        // 2q+1 (high half) of dword c/2, half c%2, for q = 0..3.
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 bq;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            bq[q] = __builtin_amdgcn_perm(f.w[2 * q + 1][c >> 1], f.w[2 * q][c >> 1], sel);
+        const bf16x8 bb = __builtin_bit_cast(bf16x8, bq);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            acc[mb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mb], bb, acc[mb][c], 0, 0, 0);
+    }
+}
+
+template <int MB, int EPI>
+__global__ __launch_bounds__(kThreads) void head_gemm_kernel(const HeadArgs a)
+{
+    __shared__ float red[kWaves][kRowBlock][kTileN + 4];
+
+    const int tile = blockIdx.x;
+    const int lane = find_lane(a.lanes, tile);
+    const int c0 = (tile - a.lanes.tile0[lane]) * kTileN;  // first column inside the lane
+    const int Vi = a.lanes.off[lane + 1] - a.lanes.off[lane];
+    const int gcol0 = a.lanes.off[lane] + c0;               // first global column
+    const int m0 = blockIdx.y * (kRowBlock * MB);
+    const int wave = threadIdx.x >> 6;
+    const int L = threadIdx.x & 63;
+    const int n = L & 15;
+    const int g = L >> 4;
+    const int H = a.H;
+
+    // Readable extents (bytes) from the tile's origin: through the last valid
+    // column of the last hidden row, rounded up to whole 16-byte vectors.
+    const uint16_t *wbase = a.lanes.w[lane] + c0;
+    const int64_t wcols = ((int64_t)(Vi - c0) + 7) & ~(int64_t)7;
+    const int64_t wbytes = H > 0 ? (((int64_t)(H - 1) * a.ldw) + wcols) * 2 : 0;
+    const int rows_here = min(a.B - m0, kRowBlock * MB);
+    const uint16_t *xbase = a.x + (int64_t)m0 * a.ldx;
+    const int64_t xbytes = H > 0 ? (((int64_t)(rows_here - 1) * a.ldx) + ((H + 7) & ~7)) * 2 : 0;
+
+    uint32_t wvo[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        wvo[r] = (uint32_t)(((int64_t)(8 * g + r) * a.ldw + 8 * n) * 2);
+    uint32_t xvo[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        xvo[mb] = (uint32_t)(((int64_t)(kRowBlock * mb + n) * a.ldx + 8 * g) * 2);
+
+    f32x4 acc[MB][8];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            acc[mb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = (H + kStepK - 1) / kStepK;
+    Frags<MB> fa, fb;
+    int s = wave;
+    if (s < nsteps)
+        load_step<MB>(fa, wbase, wbytes, xbase, xbytes, s * kStepK, a.ldw, wvo, xvo);
+    while (s < nsteps) {
+        const int s1 = s + kWaves;
+        if (s1 < nsteps)
+            load_step<MB>(fb, wbase, wbytes, xbase, xbytes, s1 * kStepK, a.ldw, wvo, xvo);
+        compute_step<MB>(fa, acc, s * kStepK, H, g);
+        s = s1;
+        if (s >= nsteps)
+            break;
+        const int s2 = s + kWaves;
+        if (s2 < nsteps)
+            load_step<MB>(fa, wbase, wbytes, xbase, xbytes, s2 * kStepK, a.ldw, wvo, xvo);
+        compute_step<MB>(fb, acc, s * kStepK, H, g);
+        s = s2;
+    }
+
+    // ---------------- epilogue, one 16-row block at a time ----------------
+    const int erow = threadIdx.x >> 4;  // 0..15: row inside the block
+    const int cg = threadIdx.x & 15;    // 8-column group inside the tile
+    const int colrel = c0 + 8 * cg;     // column inside the lane
+    const int nvalid = max(0, min(8, Vi - colrel));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        if (m0 + kRowBlock * mb >= a.B)
+            break;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            f32x4 lo = {acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+            f32x4 hi = {acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
+            *reinterpret_cast<f32x4 *>(&red[wave][4 * g + r][8 * n]) = lo;
+            *reinterpret_cast<f32x4 *>(&red[wave][4 * g + r][8 * n + 4]) = hi;
+        }
+        __syncthreads();
+        float y[8];
+        {
+            const f32x4 p0l = *reinterpret_cast<const f32x4 *>(&red[0][erow][8 * cg]);
+            const f32x4 p0h = *reinterpret_cast<const f32x4 *>(&red[0][erow][8 * cg + 4]);
+            const f32x4 p1l = *reinterpret_cast<const f32x4 *>(&red[1][erow][8 * cg]);
+            const f32x4 p1h = *reinterpret_cast<const f32x4 *>(&red[1][erow][8 * cg + 4]);
+            const f32x4 p2l = *reinterpret_cast<const f32x4 *>(&red[2][erow][8 * cg]);
+            const f32x4 p2h = *reinterpret_cast<const f32x4 *>(&red[2][erow][8 * cg + 4]);
+            const f32x4 p3l = *reinterpret_cast<const f32x4 *>(&red[3][erow][8 * cg]);
+            const f32x4 p3h = *reinterpret_cast<const f32x4 *>(&red[3][erow][8 * cg + 4]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                y[j] = ((p0l[j] + p1l[j]) + p2l[j]) + p3l[j];
+                y[j + 4] = ((p0h[j] + p1h[j]) + p2h[j]) + p3h[j];
+            }
+        }
+        __syncthreads();  // LDS free for the next block
+
+        const int b = m0 + kRowBlock * mb + erow;
+        const bool rowok = b < a.B;
+
+        if (EPI == kEpiShard || EPI == kEpiPairLseOut) {
+            float *dst;
+            if (EPI == kEpiShard)
+                dst = a.lanes.shard[lane] + (int64_t)b * a.lanes.shard_ld[lane] + colrel;
+            else
+                dst = a.out + (int64_t)b * a.ldo + gcol0 + 8 * cg;
+            if (rowok) {
+                if (nvalid == 8 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                    *reinterpret_cast<f32x4 *>(dst) = f32x4{y[0], y[1], y[2], y[3]};
+                    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{y[4], y[5], y[6], y[7]};
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (j < nvalid)
+                            dst[j] = y[j];
+                }
+            }
+        }
+        if (EPI != kEpiShard) {
+            // (max, lowest index) over the thread's columns, ascending.
+            float bv = -INFINITY;
+            int bi = INT_MAX;
+            if (nvalid > 0) {
+                bv = y[0];
+                bi = gcol0 + 8 * cg;
+            }
+#pragma unroll
+            for (int j = 1; j < 8; ++j)
+                if (j < nvalid && y[j] > bv) {
+                    bv = y[j];
+                    bi = gcol0 + 8 * cg + j;
+                }
+            // across the 16 threads of this row (one 16-lane row of the wave)
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 16);
+                const int oi = __shfl_xor(bi, o, 16);
+                if (better(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            float se = 0.f;
+            if (EPI != kEpiPair) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (j < nvalid)
+                        se += __expf(y[j] - bv);
+#pragma unroll
+                for (int o = 8; o >= 1; o >>= 1)
+                    se += __shfl_xor(se, o, 16);
+            }
+            if (cg == 0 && rowok) {
+                const int64_t idx = (int64_t)b * a.T + tile;
+                a.pair[idx] = make_int2(__float_as_int(bv), bi);
+                if (EPI != kEpiPair)
+                    a.mse[idx] = make_float2(bv, se);
+            }
+        }
+    }
+}
+
+// One workgroup per row: fold the per-tile results lane by lane.
+__global__ __launch_bounds__(kThreads) void combine_kernel(const int2 *pair, const float2 *mse,
+                                                           const LaneTable lanes, int T,
+                                                           int32_t *ids, float *lse,
+                                                           float *sel_lp)
+{
+    __shared__ float wv[kWaves], wm[kWaves], ws[kWaves];
+    __shared__ int wi[kWaves];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int L = tid & 63, wave = tid >> 6;
+    float rv = -INFINITY, rm = -INFINITY, rs = 0.f;
+    int ri = INT_MAX;
+    for (int lane = 0; lane < lanes.k; ++lane) {
+        const int t0 = lanes.tile0[lane], t1 = lanes.tile0[lane + 1];
+        float bv = -INFINITY, m = -INFINITY, s = 0.f;
+        int bi = INT_MAX;
+        for (int t = t0 + tid; t < t1; t += kThreads) {
+            const int2 p = pair[(int64_t)b * T + t];
+            const float pv = __int_as_float(p.x);
+            if (better(pv, p.y, bv, bi)) {
+                bv = pv;
+                bi = p.y;
+            }
+            if (mse) {
+                const float2 q = mse[(int64_t)b * T + t];
+                lse_merge(m, s, q.x, q.y);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (better(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+            }
+            const float om = __shfl_xor(m, o, 64);
+            const float os = __shfl_xor(s, o, 64);
+            lse_merge(m, s, om, os);
+        }
+        if (L == 0) {
+            wv[wave] = bv;
+            wi[wave] = bi;
+            wm[wave] = m;
+            ws[wave] = s;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float lv = -INFINITY, lm = -INFINITY, ls = 0.f;
+            int li = INT_MAX;
+            for (int w = 0; w < kWaves; ++w) {
+                if (better(wv[w], wi[w], lv, li)) {
+                    lv = wv[w];
+                    li = wi[w];
+                }
+                lse_merge(lm, ls, wm[w], ws[w]);
+            }
+            // lanes in ascending order: a later lane wins only if strictly
+            // larger or equal with a lower index (never, indices ascend).
+            if (better(lv, li, rv, ri)) {
+                rv = lv;
+                ri = li;
+            }
+            lse_merge(rm, rs, lm, ls);
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        ids[b] = ri;
+        const float l = rm + __logf(rs);
+        if (lse)
+            lse[b] = l;
+        if (sel_lp)
+            sel_lp[b] = rv - l;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void normalize_kernel(float *lp, int64_t ld,
+                                                             const float *lse, int V)
+{
+    const int b = blockIdx.y;
+    const int col = (blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (col >= V)
+        return;
+    const float l = lse[b];
+    float *p = lp + (int64_t)b * ld + col;
+    if (col + 4 <= V && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+        f32x4 v = *reinterpret_cast<f32x4 *>(p);
+        v -= l;
+        *reinterpret_cast<f32x4 *>(p) = v;
+    } else {
+        for (int j = 0; j < 4 && col + j < V; ++j)
+            p[j] -= l;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void reconstruct_kernel(const LaneTable lanes,
+                                                               float *logits, int64_t ldl)
+{
+    const int lane = blockIdx.z;
+    const int b = blockIdx.y;
+    const int Vi = lanes.off[lane + 1] - lanes.off[lane];
+    const int col = (blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (col >= Vi)
+        return;
+    const float *src = lanes.shard[lane] + (int64_t)b * lanes.shard_ld[lane] + col;
+    float *dst = logits + (int64_t)b * ldl + lanes.off[lane] + col;
+    if (col + 4 <= Vi && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        *reinterpret_cast<f32x4 *>(dst) = *reinterpret_cast<const f32x4 *>(src);
+    } else {
+        for (int j = 0; j < 4 && col + j < Vi; ++j)
+            dst[j] = src[j];
+    }
+}
+
+// Partial (max, lowest index) over a chunk of kArgmaxChunk columns of a row.
+__global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float *logits, int64_t ldl,
+                                                              int V, int nchunks, int2 *partial)
+{
+    __shared__ float wv[kWaves];
+    __shared__ int wi[kWaves];
+    const int b = blockIdx.y;
+    const int c0 = blockIdx.x * kArgmaxChunk;
+    const int c1 = min(V, c0 + kArgmaxChunk);
+    const float *row = logits + (int64_t)b * ldl;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int c = c0 + 4 * threadIdx.x; c < c1; c += 4 * kThreads) {
+        float v[4];
+        if (c + 4 <= c1 && (reinterpret_cast<uintptr_t>(row + c) & 15) == 0) {
+            const f32x4 q = *reinterpret_cast<const f32x4 *>(row + c);
+            v[0] = q[0], v[1] = q[1], v[2] = q[2], v[3] = q[3];
+        } else {
+            for (int j = 0; j < 4; ++j)
+                v[j] = c + j < c1 ? row[c + j] : -INFINITY;
+        }
+        for (int j = 0; j < 4; ++j)
+            if (c + j < c1 && better(v[j], c + j, bv, bi)) {
+                bv = v[j];
+                bi = c + j;
+            }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    const int L = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (L == 0) {
+        wv[wave] = bv;
+        wi[wave] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kWaves; ++w)
+            if (better(wv[w], wi[w], bv, bi)) {
+                bv = wv[w];
+                bi = wi[w];
+            }
+        partial[(int64_t)b * nchunks + blockIdx.x] = make_int2(__float_as_int(bv), bi);
+    }
+}
+
+template <int MB>
+hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
+{
+    const int rows_per_group = kRowBlock * MB;
+    dim3 grid(a.T, (a.B + rows_per_group - 1) / rows_per_group);
+    switch (epi) {
+    case kEpiPair:
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPair>), grid, dim3(kThreads), 0, s, a);
+        break;
+    case kEpiPairLse:
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPairLse>), grid, dim3(kThreads), 0, s, a);
+        break;
+    case kEpiPairLseOut:
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPairLseOut>), grid, dim3(kThreads), 0, s, a);
+        break;
+    case kEpiShard:
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiShard>), grid, dim3(kThreads), 0, s, a);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s)
+{
+    if (a.B <= 0 || a.T <= 0)
+        return hipSuccess;
+    const int blocks = (a.B + kRowBlock - 1) / kRowBlock;
+    if (blocks <= 1)
+        return launch_mb<1>(a, epi, s);
+    if (blocks == 2)
+        return launch_mb<2>(a, epi, s);
+    return launch_mb<4>(a, epi, s);
+}
+
+hipError_t launch_combine(const int2 *pair, const float2 *mse, const LaneTable &lanes,
+                          int32_t B, int32_t T, int32_t *ids, float *lse, float *sel_lp,
+                          hipStream_t s)
+{
+    if (B <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(combine_kernel, dim3(B), dim3(kThreads), 0, s, pair, mse, lanes, T, ids,
+                       lse, sel_lp);
+    return hipGetLastError();
+}
+
+hipError_t launch_normalize(float *lp, int64_t ld, const float *lse, int32_t B, int32_t V,
+                            hipStream_t s)
+{
+    if (B <= 0 || V <= 0)
+        return hipSuccess;
+    dim3 grid((V + 4 * kThreads - 1) / (4 * kThreads), B);
+    hipLaunchKernelGGL(normalize_kernel, grid, dim3(kThreads), 0, s, lp, ld, lse, V);
+    return hipGetLastError();
+}
+
+hipError_t launch_reconstruct(const LaneTable &lanes, int32_t B, float *logits, int64_t ldl,
+                              hipStream_t s)
+{
+    if (B <= 0)
+        return hipSuccess;
+    int maxv = 0;
+    for (int i = 0; i < lanes.k; ++i)
+        maxv = max(maxv, lanes.off[i + 1] - lanes.off[i]);
+    dim3 grid((maxv + 4 * kThreads - 1) / (4 * kThreads), B, lanes.k);
+    hipLaunchKernelGGL(reconstruct_kernel, grid, dim3(kThreads), 0, s, lanes, logits, ldl);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_argmax(const float *logits, int64_t ldl, int32_t B, int32_t V,
+                             int2 *partial, int32_t *ids, hipStream_t s)
+{
+    if (B <= 0)
+        return hipSuccess;
+    const int nchunks = (V + kArgmaxChunk - 1) / kArgmaxChunk;
+    hipLaunchKernelGGL(row_argmax_kernel, dim3(nchunks, B), dim3(kThreads), 0, s, logits, ldl, V,
+                       nchunks, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    LaneTable one = {};
+    one.k = 1;
+    one.off[0] = 0;
+    one.off[1] = V;
+    one.tile0[0] = 0;
+    one.tile0[1] = nchunks;
+    return launch_combine(partial, nullptr, one, B, nchunks, ids, nullptr, nullptr, s);
+}
+
+}  // namespace sbk

@@ -1,0 +1,302 @@
+// libsb C ABI: argument validation, workspace layout and kernel dispatch.
+//
+// Follows the SemBridge paper's rule that preconditions are validated before
+// anything is lowered and invalid contracts are rejected (section 3.5, static
+// validation): every check here runs on the host before the first launch, so
+// an error status means nothing was enqueued.
+#include "../../include/sb.h"
+
+#include <stdint.h>
+#include <string.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = 65535;
+constexpr size_t kRegionAlign = 256;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validation of the head descriptor (shapes, lanes, alignment, limits).
+sb_status check_desc(const sb_head_desc *d)
+{
+    if (!d || !d->lane_off || !d->w)
+        return SB_ERR_NULL;
+    if (d->B < 0 || d->H < 0 || d->V < 1)
+        return SB_ERR_SHAPE;
+    if (d->k < 1 || d->k > SB_MAX_LANES)
+        return SB_ERR_LANES;
+    if (d->lane_off[0] != 0 || d->lane_off[d->k] != d->V)
+        return SB_ERR_LANES;
+    int64_t maxv = 0;
+    for (int i = 0; i < d->k; ++i) {
+        if (d->lane_off[i + 1] <= d->lane_off[i])
+            return SB_ERR_LANES;
+        const int64_t vi = (int64_t)d->lane_off[i + 1] - d->lane_off[i];
+        if (vi > maxv)
+            maxv = vi;
+    }
+    if (d->B > 0 && d->H > 0) {
+        if (!d->x)
+            return SB_ERR_NULL;
+        for (int i = 0; i < d->k; ++i)
+            if (!d->w[i])
+                return SB_ERR_NULL;
+    }
+    if (d->ldx < d->H || d->ldw < maxv)
+        return SB_ERR_SHAPE;
+    if (d->B > 0 && d->H > 0) {
+        if (!aligned16(d->x) || (d->ldx % 8) != 0 || (d->ldw % 8) != 0)
+            return SB_ERR_ALIGN;
+        for (int i = 0; i < d->k; ++i)
+            if (!aligned16(d->w[i]))
+                return SB_ERR_ALIGN;
+    }
+    if (d->B > kMaxRows)
+        return SB_ERR_UNSUPPORTED;
+    // Per-step buffer offsets are 32-bit: 32 hidden rows of a shard and 64
+    // rows of x must span less than 4 GiB.
+    if ((int64_t)(sbk::kStepK + 8) * d->ldw * 2 >= ((int64_t)1 << 32) ||
+        (int64_t)(sbk::kRowBlock * sbk::kMaxMB) * d->ldx * 2 >= ((int64_t)1 << 32))
+        return SB_ERR_UNSUPPORTED;
+    return SB_OK;
+}
+
+int lane_width(const sb_head_desc *d, int i) { return d->lane_off[i + 1] - d->lane_off[i]; }
+
+int shard_ld(int vi) { return (vi + 3) & ~3; }
+
+struct Layout {
+    int T = 0;            // total tiles
+    int nchunks = 0;      // full-logit argmax chunks per row
+    size_t pair = 0, mse = 0, shard[SB_MAX_LANES] = {}, partial = 0;
+    size_t total = 0;
+};
+
+Layout layout(const sb_head_desc *d, int surface)
+{
+    Layout L;
+    for (int i = 0; i < d->k; ++i)
+        L.T += (lane_width(d, i) + sbk::kTileN - 1) / sbk::kTileN;
+    L.nchunks = (d->V + sbk::kArgmaxChunk - 1) / sbk::kArgmaxChunk;
+    const size_t B = (size_t)d->B;
+    size_t at = 0;
+    if (B == 0)
+        return L;
+    switch (surface) {
+    case SB_SURF_TOKENS:
+        L.pair = at;
+        at = align_up(at + B * L.T * sizeof(int2), kRegionAlign);
+        break;
+    case SB_SURF_LOGPROBS:
+    case SB_SURF_LOGPROBS_FULL:
+        L.pair = at;
+        at = align_up(at + B * L.T * sizeof(int2), kRegionAlign);
+        L.mse = at;
+        at = align_up(at + B * L.T * sizeof(float2), kRegionAlign);
+        break;
+    case SB_SURF_FULL_LOGITS:
+        for (int i = 0; i < d->k; ++i) {
+            L.shard[i] = at;
+            at = align_up(at + B * (size_t)shard_ld(lane_width(d, i)) * sizeof(float),
+                          kRegionAlign);
+        }
+        L.partial = at;
+        at = align_up(at + B * L.nchunks * sizeof(int2), kRegionAlign);
+        break;
+    default:
+        break;
+    }
+    L.total = at;
+    return L;
+}
+
+void fill_lanes(const sb_head_desc *d, sbk::LaneTable &t)
+{
+    memset(&t, 0, sizeof t);
+    t.k = d->k;
+    int tiles = 0;
+    for (int i = 0; i < d->k; ++i) {
+        t.w[i] = static_cast<const uint16_t *>(d->w[i]);
+        t.off[i] = d->lane_off[i];
+        t.tile0[i] = tiles;
+        tiles += (lane_width(d, i) + sbk::kTileN - 1) / sbk::kTileN;
+    }
+    t.off[d->k] = d->lane_off[d->k];
+    t.tile0[d->k] = tiles;
+}
+
+void fill_args(const sb_head_desc *d, const Layout &L, sbk::HeadArgs &a)
+{
+    fill_lanes(d, a.lanes);
+    a.x = static_cast<const uint16_t *>(d->x);
+    a.ldx = d->ldx;
+    a.ldw = d->ldw;
+    a.B = d->B;
+    a.H = d->H;
+    a.V = d->V;
+    a.T = L.T;
+    a.pair = nullptr;
+    a.mse = nullptr;
+    a.out = nullptr;
+    a.ldo = 0;
+}
+
+sb_status check_ws(const Layout &L, void *ws, size_t ws_bytes)
+{
+    if (L.total == 0)
+        return SB_OK;
+    if (!ws)
+        return SB_ERR_NULL;
+    if (ws_bytes < L.total)
+        return SB_ERR_WORKSPACE;
+    if (!aligned16(ws))
+        return SB_ERR_ALIGN;
+    return SB_OK;
+}
+
+template <typename T>
+T *region(void *ws, size_t off)
+{
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sb_workspace_bytes(const sb_head_desc *desc, int surface, sb_status *status)
+{
+    sb_status st = check_desc(desc);
+    if (st == SB_OK && (surface < SB_SURF_TOKENS || surface > SB_SURF_FULL_LOGITS))
+        st = SB_ERR_SHAPE;
+    if (status)
+        *status = st;
+    if (st != SB_OK)
+        return 0;
+    return layout(desc, surface).total;
+}
+
+sb_status sb_project_tokens(const sb_head_desc *desc, int32_t *ids, void *ws, size_t ws_bytes,
+                            void *stream)
+{
+    sb_status st = check_desc(desc);
+    if (st != SB_OK)
+        return st;
+    if (desc->B == 0)
+        return SB_OK;
+    if (!ids)
+        return SB_ERR_NULL;
+    const Layout L = layout(desc, SB_SURF_TOKENS);
+    if ((st = check_ws(L, ws, ws_bytes)) != SB_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    sbk::HeadArgs a;
+    fill_args(desc, L, a);
+    a.pair = region<int2>(ws, L.pair);
+    if (sbk::launch_head_gemm(a, sbk::kEpiPair, s) != hipSuccess)
+        return SB_ERR_HIP;
+    if (sbk::launch_combine(a.pair, nullptr, a.lanes, a.B, a.T, ids, nullptr, nullptr, s) !=
+        hipSuccess)
+        return SB_ERR_HIP;
+    return SB_OK;
+}
+
+sb_status sb_project_logprobs(const sb_head_desc *desc, int32_t *ids, float *lse, float *sel_lp,
+                              float *logprobs, int64_t ldlp, void *ws, size_t ws_bytes,
+                              void *stream)
+{
+    sb_status st = check_desc(desc);
+    if (st != SB_OK)
+        return st;
+    if (desc->B == 0)
+        return SB_OK;
+    if (!ids || !lse)
+        return SB_ERR_NULL;
+    if (logprobs) {
+        if (ldlp < desc->V)
+            return SB_ERR_SHAPE;
+        if (!aligned16(logprobs) || (ldlp % 4) != 0)
+            return SB_ERR_ALIGN;
+    }
+    const Layout L = layout(desc, logprobs ? SB_SURF_LOGPROBS_FULL : SB_SURF_LOGPROBS);
+    if ((st = check_ws(L, ws, ws_bytes)) != SB_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    sbk::HeadArgs a;
+    fill_args(desc, L, a);
+    a.pair = region<int2>(ws, L.pair);
+    a.mse = region<float2>(ws, L.mse);
+    a.out = logprobs;
+    a.ldo = ldlp;
+    if (sbk::launch_head_gemm(a, logprobs ? sbk::kEpiPairLseOut : sbk::kEpiPairLse, s) !=
+        hipSuccess)
+        return SB_ERR_HIP;
+    if (sbk::launch_combine(a.pair, a.mse, a.lanes, a.B, a.T, ids, lse, sel_lp, s) != hipSuccess)
+        return SB_ERR_HIP;
+    if (logprobs && sbk::launch_normalize(logprobs, ldlp, lse, a.B, a.V, s) != hipSuccess)
+        return SB_ERR_HIP;
+    return SB_OK;
+}
+
+sb_status sb_full_logits(const sb_head_desc *desc, float *logits, int64_t ldl, int32_t *ids,
+                         void *ws, size_t ws_bytes, void *stream)
+{
+    sb_status st = check_desc(desc);
+    if (st != SB_OK)
+        return st;
+    if (desc->B == 0)
+        return SB_OK;
+    if (!logits)
+        return SB_ERR_NULL;
+    if (ldl < desc->V)
+        return SB_ERR_SHAPE;
+    if (!aligned16(logits) || (ldl % 4) != 0)
+        return SB_ERR_ALIGN;
+    const Layout L = layout(desc, SB_SURF_FULL_LOGITS);
+    if ((st = check_ws(L, ws, ws_bytes)) != SB_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    sbk::HeadArgs a;
+    fill_args(desc, L, a);
+    for (int i = 0; i < desc->k; ++i) {
+        a.lanes.shard[i] = region<float>(ws, L.shard[i]);
+        a.lanes.shard_ld[i] = shard_ld(lane_width(desc, i));
+    }
+    if (sbk::launch_head_gemm(a, sbk::kEpiShard, s) != hipSuccess)
+        return SB_ERR_HIP;
+    if (sbk::launch_reconstruct(a.lanes, a.B, logits, ldl, s) != hipSuccess)
+        return SB_ERR_HIP;
+    if (ids && sbk::launch_row_argmax(logits, ldl, a.B, a.V, region<int2>(ws, L.partial), ids,
+                                      s) != hipSuccess)
+        return SB_ERR_HIP;
+    return SB_OK;
+}
+
+const char *sb_status_string(sb_status status)
+{
+    switch (status) {
+    case SB_OK:
+        return "ok";
+    case SB_ERR_NULL:
+        return "a required pointer is NULL";
+    case SB_ERR_SHAPE:
+        return "invalid shape or leading dimension";
+    case SB_ERR_LANES:
+        return "invalid lane count or lane offsets";
+    case SB_ERR_ALIGN:
+        return "pointer or leading dimension not aligned";
+    case SB_ERR_WORKSPACE:
+        return "workspace too small";
+    case SB_ERR_UNSUPPORTED:
+        return "size beyond the supported limits";
+    case SB_ERR_HIP:
+        return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -155,20 +155,34 @@ def near_tie_cols(lane_off):
     return pairs
 
 
-def make_workload(name, seed=0, B=None):
+def workload_weight(name, seed=0):
+    """The unplanted head weight of a named workload (workloads with the same
+    H, V, sigma and seed share it)."""
+    _, H, V, _, sw, _ = WORKLOADS[name]
+    return draw_weight(H, V, sw, seed)
+
+
+def make_workload(name, seed=0, B=None, w=None):
     """Inputs of a named workload.
 
     Returns a dict: x (uint16 [B,H]), w (uint16 [H,V]), lane_off (list of
     k+1 ints), name, B, H, V, k, planted (list of (row, a, b) near-tie or tie
     plants).  ``B`` overrides the row count (the large-vocab sweep runs
-    B in {1, 8, 16}).
+    B in {1, 8, 16}).  ``w`` may pass the unplanted weight from
+    ``workload_weight`` to skip drawing it again; it is never modified
+    (workloads that plant ties work on a copy).
     """
     if name not in WORKLOADS:
         raise KeyError(name)
     B0, H, V, k, sw, rms = WORKLOADS[name]
     B = B0 if B is None else int(B)
     x = draw_hidden(B, H, seed, rms_norm=rms)
-    w = draw_weight(H, V, sw, seed)
+    if w is None:
+        w = draw_weight(H, V, sw, seed)
+    else:
+        if w.shape != (H, V) or w.dtype != np.uint16:
+            raise ValueError("weight does not match the workload")
+        w = w.copy() if (name in ("tiny", "large_vocab")) else w
     lane_off = equal_lanes(V, k)
     planted = []
     if name == "tiny":

@@ -1,0 +1,203 @@
+"""Thin Python binding of libsb (include/sb.h): argument marshalling only.
+
+Every step of the head runs in libsb's HIP kernels.  PyTorch provides device
+memory and the stream; this module builds the C descriptor from tensors,
+allocates the workspace through torch when none is given, and raises
+``SbError`` on a non-zero status.  There is no fallback: if libsb.so is
+missing, loading fails with an error.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsb.so")
+
+SB_OK = 0
+SB_ERR_NULL = -1
+SB_ERR_SHAPE = -2
+SB_ERR_LANES = -3
+SB_ERR_ALIGN = -4
+SB_ERR_WORKSPACE = -5
+SB_ERR_UNSUPPORTED = -6
+SB_ERR_HIP = -7
+
+SB_SURF_TOKENS = 0
+SB_SURF_LOGPROBS = 1
+SB_SURF_LOGPROBS_FULL = 2
+SB_SURF_FULL_LOGITS = 3
+
+SB_MAX_LANES = 64
+
+EXPORTS = ("sb_workspace_bytes", "sb_project_tokens", "sb_project_logprobs",
+           "sb_full_logits", "sb_status_string")
+
+
+class SbError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class sb_head_desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("V", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("lane_off", ctypes.POINTER(ctypes.c_int32)),
+        ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
+        ("w", ctypes.POINTER(ctypes.c_void_p)), ("ldw", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libsb.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"libsb.so not found at {LIB_PATH}; build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(sb_head_desc)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    L.sb_workspace_bytes.restype = sz
+    L.sb_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    L.sb_project_tokens.restype = ctypes.c_int
+    L.sb_project_tokens.argtypes = [P, vp, vp, sz, vp]
+    L.sb_project_logprobs.restype = ctypes.c_int
+    L.sb_project_logprobs.argtypes = [P, vp, vp, vp, vp, i64, vp, sz, vp]
+    L.sb_full_logits.restype = ctypes.c_int
+    L.sb_full_logits.argtypes = [P, vp, i64, vp, vp, sz, vp]
+    L.sb_status_string.restype = ctypes.c_char_p
+    L.sb_status_string.argtypes = [ctypes.c_int]
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().sb_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+class Head:
+    """Descriptor of a head: hidden rows x [B, H] (bf16) and the lane shards.
+
+    ``w`` is either one [H, V] bf16 tensor (lanes are column ranges of it;
+    every lane offset must then be a multiple of 8) or a list of k tensors,
+    lane i of shape [H, V_i] with one common row stride.  ``lane_off`` holds
+    the k+1 vocab offsets.  Raw values (pointers, strides) can be overridden
+    to exercise the ABI's validation.
+    """
+
+    def __init__(self, x, w, lane_off, *, B=None, H=None, V=None, ldx=None,
+                 ldw=None, x_ptr=None, w_ptrs=None):
+        self.x = x
+        self.w = w
+        off = [int(o) for o in lane_off]
+        self.lane_off = off
+        k = len(off) - 1
+        self._off = (ctypes.c_int32 * max(1, k + 1))(*off)
+        if isinstance(w, (list, tuple)):
+            ptrs = [t.data_ptr() for t in w]
+            stride = w[0].stride(0) if len(w) else 0
+        else:
+            base = w.data_ptr()
+            ptrs = [base + 2 * off[i] for i in range(k)]
+            stride = w.stride(0)
+        if w_ptrs is not None:
+            ptrs = list(w_ptrs)
+        self._w = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+        self.desc = sb_head_desc(
+            B=x.shape[0] if B is None else B,
+            H=x.shape[1] if H is None else H,
+            V=off[-1] if V is None else V,
+            k=k,
+            lane_off=self._off,
+            x=x.data_ptr() if x_ptr is None else x_ptr,
+            ldx=x.stride(0) if ldx is None else ldx,
+            w=self._w,
+            ldw=stride if ldw is None else ldw)
+
+    @property
+    def B(self):
+        return self.desc.B
+
+    @property
+    def V(self):
+        return self.desc.V
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def sb_workspace_bytes(head, surface):
+    st = ctypes.c_int(0)
+    n = lib().sb_workspace_bytes(head.ref(), int(surface), ctypes.byref(st))
+    if st.value != SB_OK:
+        raise SbError(st.value, "sb_workspace_bytes")
+    return int(n)
+
+
+def _workspace(head, surface, ws, device):
+    if ws is not None:
+        return ws
+    n = sb_workspace_bytes(head, surface)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def _check(status, where):
+    if status != SB_OK:
+        raise SbError(status, where)
+
+
+def sb_project_tokens(head, ids, ws=None, stream=None):
+    """Token-only surface: ids (int32 [B], device) <- argmax token IDs."""
+    ws = _workspace(head, SB_SURF_TOKENS, ws, ids.device)
+    _check(lib().sb_project_tokens(head.ref(), _ptr(ids), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "sb_project_tokens")
+    return ids
+
+
+def sb_project_logprobs(head, ids, lse, sel_lp=None, logprobs=None, ws=None,
+                        stream=None):
+    """Log-probability surface: ids, lse, optional sel_lp and complete
+    fp32 log-probs [B, V] (row stride logprobs.stride(0))."""
+    surf = SB_SURF_LOGPROBS_FULL if logprobs is not None else SB_SURF_LOGPROBS
+    ws = _workspace(head, surf, ws, ids.device)
+    ld = logprobs.stride(0) if logprobs is not None else 0
+    _check(lib().sb_project_logprobs(head.ref(), _ptr(ids), _ptr(lse), _ptr(sel_lp),
+                                     _ptr(logprobs), ld, _ptr(ws), ws.numel(),
+                                     _stream(stream)), "sb_project_logprobs")
+    return ids
+
+
+def sb_full_logits(head, logits, ids=None, ws=None, stream=None):
+    """Full-logit plan: logits fp32 [B, V] (row stride logits.stride(0)),
+    optional ids."""
+    ws = _workspace(head, SB_SURF_FULL_LOGITS, ws, logits.device)
+    _check(lib().sb_full_logits(head.ref(), _ptr(logits), logits.stride(0), _ptr(ids),
+                                _ptr(ws), ws.numel(), _stream(stream)), "sb_full_logits")
+    return logits
+
+
+def to_device_bf16(bits, device="cuda"):
+    """uint16 numpy bf16 bit patterns -> torch.bfloat16 tensor on device."""
+    import numpy as np
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)

@@ -1,0 +1,150 @@
+"""The C ABI library on the host: it loads, exports every call that
+include/sb.h declares, and its validation rejects bad arguments with the
+documented status before any GPU work (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from logit_source_projection_amd import sb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "sb.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sb_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    assert header_functions() == sorted(sb.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = sb.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", sb.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in header_functions():
+        assert name in exported, name
+
+
+def test_status_strings():
+    for st in range(-7, 1):
+        s = sb.status_string(st)
+        assert s and s != "unknown status"
+    assert sb.status_string(-99) == "unknown status"
+
+
+# Fake, aligned host "device" pointers: validation never dereferences them and
+# every call below fails validation before anything is launched.
+FAKE = 1 << 20
+
+
+def fake_head(B=16, H=512, V=4096, off=(0, 2048, 4096), ldx=None, ldw=None,
+              x_ptr=FAKE, w_ptrs=None):
+    x = torch.empty(0)
+    off = list(off)
+    k = len(off) - 1
+    if w_ptrs is None:
+        w_ptrs = [FAKE + 2 * off[i] for i in range(k)]
+    return sb.Head(x, torch.empty(0), off, B=B, H=H, V=V,
+                   ldx=H if ldx is None else ldx, ldw=V if ldw is None else ldw,
+                   x_ptr=x_ptr, w_ptrs=w_ptrs)
+
+
+def ws_status(head, surface=sb.SB_SURF_TOKENS):
+    st = ctypes.c_int(123)
+    sb.lib().sb_workspace_bytes(head.ref(), surface, ctypes.byref(st))
+    return st.value
+
+
+def tokens_status(head, ids=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return sb.lib().sb_project_tokens(head.ref(), ids, ws, ws_bytes, None)
+
+
+def test_workspace_bytes_for_the_workloads():
+    h = fake_head(B=16, H=5120, V=151936, off=(0, 37984, 75968, 113952, 151936))
+    T = 4 * 297
+    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == ((16 * T * 8 + 255) // 256) * 256
+    lp = sb.sb_workspace_bytes(h, sb.SB_SURF_LOGPROBS)
+    assert lp >= 2 * 16 * T * 8
+    full = sb.sb_workspace_bytes(h, sb.SB_SURF_FULL_LOGITS)
+    assert full >= 16 * 151936 * 4
+    assert sb.sb_workspace_bytes(fake_head(B=0), sb.SB_SURF_TOKENS) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), sb.SB_ERR_SHAPE),
+    (dict(H=-5), sb.SB_ERR_SHAPE),
+    (dict(V=0, off=(0, 0)), sb.SB_ERR_SHAPE),
+    (dict(off=(0, 4096), V=4000), sb.SB_ERR_LANES),
+    (dict(off=(0, 2048, 2048, 4096)), sb.SB_ERR_LANES),
+    (dict(off=(0, 3000, 2048, 4096)), sb.SB_ERR_LANES),
+    (dict(off=(8, 2048, 4096)), sb.SB_ERR_LANES),
+    (dict(ldx=256), sb.SB_ERR_SHAPE),
+    (dict(ldw=2000), sb.SB_ERR_SHAPE),
+    (dict(ldx=516), sb.SB_ERR_ALIGN),
+    (dict(ldw=4100), sb.SB_ERR_ALIGN),
+    (dict(x_ptr=FAKE + 2), sb.SB_ERR_ALIGN),
+    (dict(w_ptrs=[FAKE, FAKE + 2 * 2047]), sb.SB_ERR_ALIGN),
+    (dict(x_ptr=0), sb.SB_ERR_NULL),
+    (dict(w_ptrs=[FAKE, 0]), sb.SB_ERR_NULL),
+    (dict(B=70000), sb.SB_ERR_UNSUPPORTED),
+    (dict(V=(1 << 31) - 8, off=(0, (1 << 31) - 8), ldw=(1 << 31) - 8), sb.SB_ERR_UNSUPPORTED),
+])
+def test_descriptor_validation(kw, status):
+    h = fake_head(**kw)
+    assert ws_status(h) == status
+    assert tokens_status(h) == status
+
+
+def test_too_many_lanes():
+    V = 8 * 65
+    off = list(range(0, V + 1, 8))
+    assert len(off) - 1 == 65
+    assert ws_status(fake_head(V=V, off=off, ldw=V)) == sb.SB_ERR_LANES
+
+
+def test_output_and_workspace_checks():
+    h = fake_head()
+    need = sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS)
+    assert tokens_status(h, ids=None) == sb.SB_ERR_NULL
+    assert tokens_status(h, ws=None) == sb.SB_ERR_NULL
+    assert tokens_status(h, ws_bytes=need - 1) == sb.SB_ERR_WORKSPACE
+    assert tokens_status(h, ws=FAKE + 4) == sb.SB_ERR_ALIGN
+    L = sb.lib()
+    # log-prob surface: lse required, logprobs stride / alignment
+    assert L.sb_project_logprobs(h.ref(), FAKE, None, None, None, 0, FAKE, 1 << 30, None) == sb.SB_ERR_NULL
+    assert L.sb_project_logprobs(h.ref(), FAKE, FAKE, None, FAKE, 4000, FAKE, 1 << 30, None) == sb.SB_ERR_SHAPE
+    assert L.sb_project_logprobs(h.ref(), FAKE, FAKE, None, FAKE, 4098, FAKE, 1 << 30, None) == sb.SB_ERR_ALIGN
+    assert L.sb_project_logprobs(h.ref(), FAKE, FAKE, None, FAKE + 8, 4096, FAKE, 1 << 30, None) == sb.SB_ERR_ALIGN
+    # full-logit plan
+    assert L.sb_full_logits(h.ref(), None, 4096, None, FAKE, 1 << 30, None) == sb.SB_ERR_NULL
+    assert L.sb_full_logits(h.ref(), FAKE, 4095, None, FAKE, 1 << 30, None) == sb.SB_ERR_SHAPE
+    assert L.sb_full_logits(h.ref(), FAKE, 4098, None, FAKE, 1 << 30, None) == sb.SB_ERR_ALIGN
+    need_full = sb.sb_workspace_bytes(h, sb.SB_SURF_FULL_LOGITS)
+    assert L.sb_full_logits(h.ref(), FAKE, 4096, None, FAKE, need_full - 1, None) == sb.SB_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_noop():
+    h = fake_head(B=0, x_ptr=0)
+    # nothing to do: no pointer is needed and nothing is launched
+    assert tokens_status(h, ids=None, ws=None, ws_bytes=0) == sb.SB_OK
+    L = sb.lib()
+    assert L.sb_project_logprobs(h.ref(), None, None, None, None, 0, None, 0, None) == sb.SB_OK
+    assert L.sb_full_logits(h.ref(), None, 0, None, None, 0, None) == sb.SB_OK
+
+
+def test_binding_raises_on_error():
+    h = fake_head(B=-1)
+    with pytest.raises(sb.SbError) as e:
+        sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS)
+    assert e.value.status == sb.SB_ERR_SHAPE

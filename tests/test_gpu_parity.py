@@ -1,0 +1,175 @@
+"""GPU parity: libsb's HIP path against the CPU oracle, through the C ABI.
+
+Small cases run the oracle on every output; they span several 128-column
+tiles, ragged lane widths, ragged hidden sizes and more than one 64-row
+group.  Edge cases: empty hidden size, zero rows, one-hot rows, exact ties,
+power-of-two scaling, non-finite padding that must never be read, lane-count
+invariance, run-to-run determinism.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from logit_source_projection_amd import inputs, sb
+from tests.gpu_common import check_against_oracle, check_internal, run_surfaces, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(d, **up):
+    print(f"case {d['name']} B={d['B']} H={d['H']} V={d['V']} lanes={d['lane_off']} {up}",
+          flush=True)
+    head = upload(d, **up)
+    g = run_surfaces(head)
+    check_internal(g)
+    z = oracle.logits(d["x"], d["w"])
+    r = check_against_oracle(g, z, d["lane_off"])
+    return g, z, r
+
+
+def test_tiny_workload_with_forced_tie(require_gpu):
+    d = inputs.make_workload("tiny")
+    g, z, r = _case(d)
+    row, a, b = d["planted"][0]
+    # identical columns give bit-identical fp32 logits: a true tie on the GPU
+    assert g["logits"][row, a] == g["logits"][row, b]
+    assert g["ids_tok"][row] == a == 1000
+    assert np.array_equal(g["ids_tok"], r["ids"])
+
+
+SMALL = [
+    # B, H, V, lane offsets, separate lane allocations
+    (16, 512, 3000, [0, 1000, 1001, 2999, 3000], True),
+    (1, 256, 4096, [0, 4096], False),
+    (7, 200, 1288, [0, 640, 1288], False),
+    (17, 96, 2056, [0, 1024, 2056], False),
+    (33, 1000, 777, [0, 300, 777], True),
+    (64, 4096, 2048, [0, 1024, 2048], False),
+    (65, 128, 1000, [0, 13, 500, 1000], True),
+    (130, 72, 1536, [0, 512, 1024, 1536], False),
+    (5, 8, 100, [0, 50, 100], True),
+    (3, 40, 129, [0, 129], True),
+]
+
+
+@pytest.mark.parametrize("B,H,V,off,sep", SMALL)
+def test_small_heads(require_gpu, B, H, V, off, sep):
+    d = inputs.make_random(B, H, V, off, seed=B * 7 + H)
+    _case(d, lanes_separate=sep)
+
+
+def test_non_finite_padding_is_never_read(require_gpu):
+    B, H, V = 9, 100, 700
+    off = [0, 200, 433, 700]
+    d = inputs.make_random(B, H, V, off, seed=5)
+    g, _, _ = _case(d, lanes_separate=True, pad_w=24, pad_x=28)
+    g2 = run_surfaces(upload(d))
+    assert np.array_equal(g["logits"], g2["logits"])
+
+
+def test_empty_hidden_size(require_gpu):
+    B, V = 3, 1000
+    x = torch.empty((B, 0), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((0, V), dtype=torch.bfloat16, device="cuda")
+    head = sb.Head(x, w, [0, 504, 1000], ldx=8, ldw=1000)
+    g = run_surfaces(head)
+    check_internal(g)
+    assert np.all(g["logits"] == 0.0)
+    assert np.all(g["ids_tok"] == 0)
+    assert np.allclose(g["lse"], math.log(V), rtol=1e-6)
+
+
+def test_empty_batch(require_gpu):
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    head = sb.Head(x, w, [0, 256])
+    ids = torch.empty((0,), dtype=torch.int32, device="cuda")
+    sb.sb_project_tokens(head, ids)
+    torch.cuda.synchronize()
+
+
+def test_zero_and_one_hot_rows(require_gpu):
+    B, H, V = 6, 320, 5000
+    off = [0, 2504, 5000]
+    d = inputs.make_random(B, H, V, off, seed=9)
+    x = d["x"]
+    x[0, :] = 0
+    one = np.uint16(inputs.f32_to_bf16_bits(np.float32(1.0)))
+    for b, h in [(1, 0), (2, 177), (3, 319)]:
+        x[b, :] = 0
+        x[b, h] = one
+    g, z, r = _case(d)
+    assert np.all(g["logits"][0] == 0.0) and g["ids_tok"][0] == 0
+    assert abs(float(g["lse"][0]) - math.log(V)) <= 1e-5
+    for b, h in [(1, 0), (2, 177), (3, 319)]:
+        wrow = inputs.bf16_bits_to_f32(d["w"][h])
+        assert np.array_equal(g["logits"][b], wrow), (b, h)
+
+
+def test_power_of_two_scaling(require_gpu):
+    B, H, V = 8, 512, 3072
+    off = [0, 1024, 3072]
+    d = inputs.make_random(B, H, V, off, seed=10)
+    g1 = run_surfaces(upload(d))
+    x2 = d["x"].copy()
+    nz = (x2 & 0x7FFF) != 0
+    x2[nz] += np.uint16(1 << 7)
+    d2 = dict(d, x=x2)
+    g2 = run_surfaces(upload(d2))
+    assert np.array_equal(g2["logits"], 2.0 * g1["logits"])
+    assert np.array_equal(g2["ids_tok"], g1["ids_tok"])
+
+
+def test_exact_ties_across_and_within_lanes(require_gpu):
+    B, H, V = 4, 256, 4096
+    off = [0, 1024, 2048, 3072, 4096]
+    d = inputs.make_random(B, H, V, off, seed=11)
+    inputs.plant_equal_columns(d["x"], d["w"], 0, (3500, 2500, 700), 9.0)
+    inputs.plant_equal_columns(d["x"], d["w"], 2, (1500, 1030), 9.0)
+    inputs.plant_equal_columns(d["x"], d["w"], 3, (1023, 1024), 9.0)  # lane boundary
+    g, z, r = _case(d)
+    assert list(g["ids_tok"][[0, 2, 3]]) == [700, 1030, 1023]
+
+
+def test_lane_count_invariance(require_gpu):
+    B, H, V = 16, 1024, 8192
+    d = inputs.make_random(B, H, V, [0, V], seed=12)
+    outs = []
+    for k in (1, 2, 4, 8):
+        d["lane_off"] = inputs.equal_lanes(V, k)
+        outs.append(run_surfaces(upload(d)))
+    for o in outs[1:]:
+        assert np.array_equal(o["logits"], outs[0]["logits"])
+        assert np.array_equal(o["ids_tok"], outs[0]["ids_tok"])
+
+
+def test_repeated_calls_are_bitwise_identical(require_gpu):
+    d = inputs.make_random(24, 640, 6000, [0, 3000, 6000], seed=13)
+    head = upload(d)
+    first = run_surfaces(head)
+    for _ in range(3):
+        again = run_surfaces(head)
+        for key in ("ids_tok", "ids_lp", "ids_r0", "lse", "sel_lp", "logits", "logprobs"):
+            assert np.array_equal(first[key], again[key]), key
+
+
+def test_workspace_reuse_across_shapes(require_gpu):
+    # one workspace, a large call then a small one on the same stream
+    big = inputs.make_random(40, 256, 9000, [0, 4500, 9000], seed=14)
+    small = inputs.make_random(3, 256, 1000, [0, 1000], seed=15)
+    hb, hs = upload(big), upload(small)
+    n = sb.sb_workspace_bytes(hb, sb.SB_SURF_LOGPROBS)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for d, h in ((big, hb), (small, hs)):
+        ids = torch.empty(d["B"], dtype=torch.int32, device="cuda")
+        lse = torch.empty(d["B"], dtype=torch.float32, device="cuda")
+        sb.sb_project_logprobs(h, ids, lse, ws=ws)
+        torch.cuda.synchronize()
+        z = oracle.logits(d["x"], d["w"])
+        r = oracle.project(z, d["lane_off"])
+        ok = ~r["near_tie"]
+        assert np.array_equal(ids.cpu().numpy()[ok], r["ids"][ok])
+        assert np.allclose(lse.cpu().numpy(), r["lse"], rtol=1e-4)
