@@ -52,8 +52,10 @@ def run_surfaces(head, device="cuda", full_logprobs=True):
     ids_r0 = torch.full((B,), -1, dtype=torch.int32, device=device)
     lse = torch.full((B,), float("nan"), dtype=torch.float32, device=device)
     sel = torch.full((B,), float("nan"), dtype=torch.float32, device=device)
-    lp = torch.full((B, V), float("nan"), dtype=torch.float32, device=device) if full_logprobs else None
-    logits = torch.full((B, V), float("nan"), dtype=torch.float32, device=device)
+    ldv = (V + 3) // 4 * 4  # fp32 outputs need a row stride that is a multiple of 4
+    lp = (torch.full((B, ldv), float("nan"), dtype=torch.float32, device=device)[:, :V]
+          if full_logprobs else None)
+    logits = torch.full((B, ldv), float("nan"), dtype=torch.float32, device=device)[:, :V]
     sb.sb_project_tokens(head, ids_tok)
     sb.sb_project_logprobs(head, ids_lp, lse, sel, lp)
     sb.sb_full_logits(head, logits, ids_r0)

@@ -66,7 +66,7 @@ def test_non_finite_padding_is_never_read(require_gpu):
     off = [0, 200, 433, 700]
     d = inputs.make_random(B, H, V, off, seed=5)
     g, _, _ = _case(d, lanes_separate=True, pad_w=24, pad_x=28)
-    g2 = run_surfaces(upload(d))
+    g2 = run_surfaces(upload(d, lanes_separate=True, pad_w=24, pad_x=28, pad_bits=0))
     assert np.array_equal(g["logits"], g2["logits"])
 
 
@@ -158,7 +158,7 @@ def test_repeated_calls_are_bitwise_identical(require_gpu):
 
 def test_workspace_reuse_across_shapes(require_gpu):
     # one workspace, a large call then a small one on the same stream
-    big = inputs.make_random(40, 256, 9000, [0, 4500, 9000], seed=14)
+    big = inputs.make_random(40, 256, 9008, [0, 4504, 9008], seed=14)
     small = inputs.make_random(3, 256, 1000, [0, 1000], seed=15)
     hb, hs = upload(big), upload(small)
     n = sb.sb_workspace_bytes(hb, sb.SB_SURF_LOGPROBS)
