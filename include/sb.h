@@ -39,6 +39,10 @@
  *    the default stream).  Inputs are read-only.  The workspace is scratch
  *    owned by the call until its work completes on the stream; calls that
  *    share one workspace must be ordered on one stream.
+ *  - A workspace must be ZERO-FILLED before its first use (allocate it once,
+ *    zeroed, and reuse it).  The token and log-prob calls keep completion
+ *    counters at its start; every call that completes leaves them zero, so
+ *    a workspace stays valid for later calls of any shape.
  *
  * Errors
  *  - Validation is synchronous: on any error status nothing is enqueued and
@@ -122,7 +126,7 @@ size_t sb_workspace_bytes(const sb_head_desc *desc, int surface, sb_status *stat
  * ids[b] = lowest global index of max_v z[b][v].  Each lane reduces to one
  * (max, lowest-index) result per row inside the GEMM epilogue; the per-lane
  * results are combined in ascending lane order.  The full logits are never
- * written to memory.
+ * written to memory.  One kernel launch.
  *   ids  DEVICE int32 [B]
  *   ws   DEVICE workspace of >= sb_workspace_bytes(desc, SB_SURF_TOKENS)
  *        bytes, 16-byte aligned

@@ -43,9 +43,23 @@ struct HeadArgs {
     float2 *mse;         // [B][T] {tile max, sum exp(y - tile max)}
     float *out;          // [B][ldo] fp32 logits at global columns (kEpiPairLseOut)
     int64_t ldo;
+    // Completion protocol of the token / log-prob surfaces: the workgroup
+    // that finishes a lane's last tile folds that lane, the one that finishes
+    // a row group's last lane folds the lanes into ids / lse / sel_lp.
+    uint32_t *sync;      // [row groups][k + 1] counters: zero on entry, left zero
+    int2 *lane_pair;     // [B][k] per-lane {max bits, global index}
+    float2 *lane_mse;    // [B][k] per-lane {max, sum exp(y - max)}
+    int32_t *ids;        // [B]
+    float *lse;          // [B] or null
+    float *sel_lp;       // [B] or null
 };
 
-// Launch the head GEMM with the given epilogue; MB row blocks per workgroup.
+// Rows per workgroup row group (grid y) for a batch of B rows.
+inline int rows_per_group(int B) { return B <= kRowBlock ? kRowBlock : (B <= 2 * kRowBlock ? 2 * kRowBlock : kMaxMB * kRowBlock); }
+
+// Launch the head GEMM with the given epilogue.  For every epilogue except
+// kEpiShard the launch also produces ids (and lse / sel_lp when non-null)
+// through the completion protocol.
 hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s);
 
 // Fold the (row, tile) workspaces into ids / lse / sel_lp (any may be NULL

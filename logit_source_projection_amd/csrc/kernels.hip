@@ -76,6 +76,19 @@ __device__ __forceinline__ void lse_merge(float &m1, float &s1, float m2, float 
     }
 }
 
+// Results read by another workgroup of the same launch are written through
+// to memory (system-scope relaxed atomic stores are never left dirty in an
+// XCD's L2), so publishing them needs only a wait for store completion -- no
+// L2 write-back fence in every workgroup.
+__device__ __forceinline__ void store_through(void *p, uint32_t lo, uint32_t hi)
+{
+    const uint64_t v = (uint64_t)lo | ((uint64_t)hi << 32);
+    __hip_atomic_store(static_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// All of this wave's memory operations have completed.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ int find_lane(const LaneTable &t, int tile)
 {
     int lane = 0;
@@ -149,8 +162,127 @@ __device__ __forceinline__ void compute_step(Frags<MB> &f, f32x4 (&acc)[MB][8], 
     }
 }
 
+// Completion protocol, run by every workgroup after its tile's (row, tile)
+// results are stored.  The workgroup that completes the last tile of a lane
+// (for its row group) folds that lane's tiles in a fixed order into one
+// result per row -- the paper's one int32 result per lane -- and the one that
+// completes the last lane folds the k lane results in ascending lane order.
+// Counters are left at zero for the next call on the same workspace.
 template <int MB, int EPI>
-__global__ __launch_bounds__(kThreads) void head_gemm_kernel(const HeadArgs a)
+__device__ void finish_tile(const HeadArgs &a, int lane, int m0, int rows_here)
+{
+    __shared__ int s_last;
+    const int k = a.lanes.k;
+    uint32_t *lane_ctr = a.sync + (int64_t)blockIdx.y * (k + 1) + lane;
+    uint32_t *group_ctr = a.sync + (int64_t)blockIdx.y * (k + 1) + k;
+    const int t0 = a.lanes.tile0[lane], t1 = a.lanes.tile0[lane + 1];
+
+    wait_all_memory();  // this wave's written-through results are in memory
+    __syncthreads();    // ... and every other wave's
+    if (threadIdx.x == 0) {
+        const uint32_t old = atomicAdd(lane_ctr, 1u);
+        s_last = old == (uint32_t)(t1 - t0 - 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    // acquire: drop stale cached copies before reading the lane's results
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+    constexpr int TPR = kThreads / (kRowBlock * MB);  // threads per row
+    const int r = threadIdx.x / TPR, j = threadIdx.x % TPR;
+    const int b = m0 + r;
+    const bool rowok = r < rows_here;
+    float bv = -INFINITY, m = -INFINITY, se = 0.f;
+    int bi = INT_MAX;
+    if (rowok) {
+        for (int t = t0 + j; t < t1; t += TPR) {
+            const int64_t idx = (int64_t)b * a.T + t;
+            const int2 p = a.pair[idx];
+            const float pv = __int_as_float(p.x);
+            if (better(pv, p.y, bv, bi)) {
+                bv = pv;
+                bi = p.y;
+            }
+            if (EPI != kEpiPair) {
+                const float2 q = a.mse[idx];
+                lse_merge(m, se, q.x, q.y);
+            }
+        }
+    }
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, TPR);
+        const int oi = __shfl_xor(bi, o, TPR);
+        if (better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+        if (EPI != kEpiPair) {
+            const float om = __shfl_xor(m, o, TPR);
+            const float os = __shfl_xor(se, o, TPR);
+            lse_merge(m, se, om, os);
+        }
+    }
+    if (rowok && j == 0) {
+        store_through(&a.lane_pair[(int64_t)b * k + lane], __float_as_uint(bv), (uint32_t)bi);
+        if (EPI != kEpiPair)
+            store_through(&a.lane_mse[(int64_t)b * k + lane], __float_as_uint(m),
+                          __float_as_uint(se));
+    }
+    wait_all_memory();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_store(lane_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = atomicAdd(group_ctr, 1u);
+        s_last = old == (uint32_t)(k - 1);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (threadIdx.x < rows_here) {
+        const int row = m0 + threadIdx.x;
+        float rv = -INFINITY, rm = -INFINITY, rs = 0.f;
+        int ri = INT_MAX;
+        for (int i = 0; i < k; ++i) {
+            const int2 p = a.lane_pair[(int64_t)row * k + i];
+            const float pv = __int_as_float(p.x);
+            if (better(pv, p.y, rv, ri)) {
+                rv = pv;
+                ri = p.y;
+            }
+            if (EPI != kEpiPair) {
+                const float2 q = a.lane_mse[(int64_t)row * k + i];
+                lse_merge(rm, rs, q.x, q.y);
+            }
+        }
+        a.ids[row] = ri;
+        if (EPI != kEpiPair) {
+            const float l = rm + __logf(rs);
+            if (a.lse)
+                a.lse[row] = l;
+            if (a.sel_lp)
+                a.sel_lp[row] = rv - l;
+        }
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(group_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Minimum workgroups per CU handed to the register allocator.  One row block
+// is left unconstrained (it settles at 3 waves per SIMD; squeezing it into
+// 128 registers for a 4th wave costs a third of the bandwidth); two row
+// blocks are held to 2 waves per SIMD; four row blocks need the whole
+// register file (their 128 accumulators do not fit beside two weight
+// buffers in 256 registers).
+template <int MB>
+struct Occupancy {
+    static constexpr int kBlocksPerCU = MB == 2 ? 2 : 1;
+};
+
+template <int MB, int EPI>
+__global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_gemm_kernel(const HeadArgs a)
 {
     __shared__ float red[kWaves][kRowBlock][kTileN + 4];
 
@@ -160,7 +292,9 @@ __global__ __launch_bounds__(kThreads) void head_gemm_kernel(const HeadArgs a)
     const int Vi = a.lanes.off[lane + 1] - a.lanes.off[lane];
     const int gcol0 = a.lanes.off[lane] + c0;               // first global column
     const int m0 = blockIdx.y * (kRowBlock * MB);
-    const int wave = threadIdx.x >> 6;
+    // wave index made provably wave-uniform, so that the per-step buffer
+    // resources live in scalar registers (no waterfall loops around loads)
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int L = threadIdx.x & 63;
     const int n = L & 15;
     const int g = L >> 4;
@@ -303,12 +437,14 @@ __global__ __launch_bounds__(kThreads) void head_gemm_kernel(const HeadArgs a)
             }
             if (cg == 0 && rowok) {
                 const int64_t idx = (int64_t)b * a.T + tile;
-                a.pair[idx] = make_int2(__float_as_int(bv), bi);
+                store_through(&a.pair[idx], __float_as_uint(bv), (uint32_t)bi);
                 if (EPI != kEpiPair)
-                    a.mse[idx] = make_float2(bv, se);
+                    store_through(&a.mse[idx], __float_as_uint(bv), __float_as_uint(se));
             }
         }
     }
+    if (EPI != kEpiShard)
+        finish_tile<MB, EPI>(a, lane, m0, rows_here);
 }
 
 // One workgroup per row: fold the per-tile results lane by lane.
@@ -509,12 +645,14 @@ hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s)
 {
     if (a.B <= 0 || a.T <= 0)
         return hipSuccess;
-    const int blocks = (a.B + kRowBlock - 1) / kRowBlock;
-    if (blocks <= 1)
+    switch (rows_per_group(a.B)) {
+    case kRowBlock:
         return launch_mb<1>(a, epi, s);
-    if (blocks == 2)
+    case 2 * kRowBlock:
         return launch_mb<2>(a, epi, s);
-    return launch_mb<4>(a, epi, s);
+    default:
+        return launch_mb<kMaxMB>(a, epi, s);
+    }
 }
 
 hipError_t launch_combine(const int2 *pair, const float2 *mse, const LaneTable &lanes,

@@ -72,7 +72,9 @@ int shard_ld(int vi) { return (vi + 3) & ~3; }
 struct Layout {
     int T = 0;            // total tiles
     int nchunks = 0;      // full-logit argmax chunks per row
-    size_t pair = 0, mse = 0, shard[SB_MAX_LANES] = {}, partial = 0;
+    int groups = 0;       // row groups (grid y) of the head GEMM
+    size_t sync = 0, pair = 0, mse = 0, lane_pair = 0, lane_mse = 0;
+    size_t shard[SB_MAX_LANES] = {}, partial = 0;
     size_t total = 0;
 };
 
@@ -86,17 +88,30 @@ Layout layout(const sb_head_desc *d, int surface)
     size_t at = 0;
     if (B == 0)
         return L;
+    const int rpg = sbk::rows_per_group(d->B);
+    L.groups = (d->B + rpg - 1) / rpg;
     switch (surface) {
     case SB_SURF_TOKENS:
+        // completion counters first: the region that must start zeroed
+        L.sync = at;
+        at = align_up(at + (size_t)L.groups * (d->k + 1) * sizeof(uint32_t), kRegionAlign);
         L.pair = at;
         at = align_up(at + B * L.T * sizeof(int2), kRegionAlign);
+        L.lane_pair = at;
+        at = align_up(at + B * d->k * sizeof(int2), kRegionAlign);
         break;
     case SB_SURF_LOGPROBS:
     case SB_SURF_LOGPROBS_FULL:
+        L.sync = at;
+        at = align_up(at + (size_t)L.groups * (d->k + 1) * sizeof(uint32_t), kRegionAlign);
         L.pair = at;
         at = align_up(at + B * L.T * sizeof(int2), kRegionAlign);
         L.mse = at;
         at = align_up(at + B * L.T * sizeof(float2), kRegionAlign);
+        L.lane_pair = at;
+        at = align_up(at + B * d->k * sizeof(int2), kRegionAlign);
+        L.lane_mse = at;
+        at = align_up(at + B * d->k * sizeof(float2), kRegionAlign);
         break;
     case SB_SURF_FULL_LOGITS:
         for (int i = 0; i < d->k; ++i) {
@@ -143,6 +158,12 @@ void fill_args(const sb_head_desc *d, const Layout &L, sbk::HeadArgs &a)
     a.mse = nullptr;
     a.out = nullptr;
     a.ldo = 0;
+    a.sync = nullptr;
+    a.lane_pair = nullptr;
+    a.lane_mse = nullptr;
+    a.ids = nullptr;
+    a.lse = nullptr;
+    a.sel_lp = nullptr;
 }
 
 sb_status check_ws(const Layout &L, void *ws, size_t ws_bytes)
@@ -196,11 +217,11 @@ sb_status sb_project_tokens(const sb_head_desc *desc, int32_t *ids, void *ws, si
     hipStream_t s = static_cast<hipStream_t>(stream);
     sbk::HeadArgs a;
     fill_args(desc, L, a);
+    a.sync = region<uint32_t>(ws, L.sync);
     a.pair = region<int2>(ws, L.pair);
+    a.lane_pair = region<int2>(ws, L.lane_pair);
+    a.ids = ids;
     if (sbk::launch_head_gemm(a, sbk::kEpiPair, s) != hipSuccess)
-        return SB_ERR_HIP;
-    if (sbk::launch_combine(a.pair, nullptr, a.lanes, a.B, a.T, ids, nullptr, nullptr, s) !=
-        hipSuccess)
         return SB_ERR_HIP;
     return SB_OK;
 }
@@ -228,14 +249,18 @@ sb_status sb_project_logprobs(const sb_head_desc *desc, int32_t *ids, float *lse
     hipStream_t s = static_cast<hipStream_t>(stream);
     sbk::HeadArgs a;
     fill_args(desc, L, a);
+    a.sync = region<uint32_t>(ws, L.sync);
     a.pair = region<int2>(ws, L.pair);
     a.mse = region<float2>(ws, L.mse);
+    a.lane_pair = region<int2>(ws, L.lane_pair);
+    a.lane_mse = region<float2>(ws, L.lane_mse);
+    a.ids = ids;
+    a.lse = lse;
+    a.sel_lp = sel_lp;
     a.out = logprobs;
     a.ldo = ldlp;
     if (sbk::launch_head_gemm(a, logprobs ? sbk::kEpiPairLseOut : sbk::kEpiPairLse, s) !=
         hipSuccess)
-        return SB_ERR_HIP;
-    if (sbk::launch_combine(a.pair, a.mse, a.lanes, a.B, a.T, ids, lse, sel_lp, s) != hipSuccess)
         return SB_ERR_HIP;
     if (logprobs && sbk::launch_normalize(logprobs, ldlp, lse, a.B, a.V, s) != hipSuccess)
         return SB_ERR_HIP;

@@ -154,11 +154,17 @@ def sb_workspace_bytes(head, surface):
     return int(n)
 
 
+def workspace(head, surface, device="cuda"):
+    """A zero-filled workspace for `surface` (the ABI requires a zeroed
+    workspace on first use; every call leaves it reusable)."""
+    n = sb_workspace_bytes(head, surface)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
 def _workspace(head, surface, ws, device):
     if ws is not None:
         return ws
-    n = sb_workspace_bytes(head, surface)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    return workspace(head, surface, device)
 
 
 def _check(status, where):

@@ -162,7 +162,7 @@ def test_workspace_reuse_across_shapes(require_gpu):
     small = inputs.make_random(3, 256, 1000, [0, 1000], seed=15)
     hb, hs = upload(big), upload(small)
     n = sb.sb_workspace_bytes(hb, sb.SB_SURF_LOGPROBS)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     for d, h in ((big, hb), (small, hs)):
         ids = torch.empty(d["B"], dtype=torch.int32, device="cuda")
         lse = torch.empty(d["B"], dtype=torch.float32, device="cuda")
