@@ -169,12 +169,12 @@ __device__ __forceinline__ void compute_step(Frags<MB> &f, f32x4 (&acc)[MB][8], 
 // completes the last lane folds the k lane results in ascending lane order.
 // Counters are left at zero for the next call on the same workspace.
 template <int MB, int EPI>
-__device__ void finish_tile(const HeadArgs &a, int lane, int m0, int rows_here)
+__device__ void finish_tile(const HeadArgs &a, int lane, int group, int m0, int rows_here)
 {
     __shared__ int s_last;
     const int k = a.lanes.k;
-    uint32_t *lane_ctr = a.sync + (int64_t)blockIdx.y * (k + 1) + lane;
-    uint32_t *group_ctr = a.sync + (int64_t)blockIdx.y * (k + 1) + k;
+    uint32_t *lane_ctr = a.sync + (int64_t)group * (k + 1) + lane;
+    uint32_t *group_ctr = a.sync + (int64_t)group * (k + 1) + k;
     const int t0 = a.lanes.tile0[lane], t1 = a.lanes.tile0[lane + 1];
 
     wait_all_memory();  // this wave's written-through results are in memory
@@ -273,9 +273,7 @@ __device__ void finish_tile(const HeadArgs &a, int lane, int m0, int rows_here)
 // Minimum workgroups per CU handed to the register allocator.  One row block
 // is left unconstrained (it settles at 3 waves per SIMD; squeezing it into
 // 128 registers for a 4th wave costs a third of the bandwidth); two row
-// blocks are held to 2 waves per SIMD; four row blocks need the whole
-// register file (their 128 accumulators do not fit beside two weight
-// buffers in 256 registers).
+// blocks are held to 2 waves per SIMD.
 template <int MB>
 struct Occupancy {
     static constexpr int kBlocksPerCU = MB == 2 ? 2 : 1;
@@ -286,12 +284,22 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
 {
     __shared__ float red[kWaves][kRowBlock][kTileN + 4];
 
-    const int tile = blockIdx.x;
+    // 1-D grid in blocks of 8 tiles x all row groups: the row groups of one
+    // weight tile get workgroup ids 8 apart.  Workgroups are handed to the 8
+    // XCDs round-robin, so they share one XCD's L2 and all but the first
+    // read the tile from it (a placement hint only; results do not depend on
+    // where a workgroup runs).  Ids past the last tile exit at once.
+    const int groups = (a.B + kRowBlock * MB - 1) / (kRowBlock * MB);
+    const int q = blockIdx.x >> 3;
+    const int tile = (q / groups) * 8 + (blockIdx.x & 7);
+    const int group = q - (q / groups) * groups;
+    if (tile >= a.T)
+        return;
     const int lane = find_lane(a.lanes, tile);
     const int c0 = (tile - a.lanes.tile0[lane]) * kTileN;  // first column inside the lane
     const int Vi = a.lanes.off[lane + 1] - a.lanes.off[lane];
     const int gcol0 = a.lanes.off[lane] + c0;               // first global column
-    const int m0 = blockIdx.y * (kRowBlock * MB);
+    const int m0 = group * (kRowBlock * MB);
     // wave index made provably wave-uniform, so that the per-step buffer
     // resources live in scalar registers (no waterfall loops around loads)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -444,7 +452,7 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
         }
     }
     if (EPI != kEpiShard)
-        finish_tile<MB, EPI>(a, lane, m0, rows_here);
+        finish_tile<MB, EPI>(a, lane, group, m0, rows_here);
 }
 
 // One workgroup per row: fold the per-tile results lane by lane.
@@ -618,8 +626,8 @@ __global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float *logit
 template <int MB>
 hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
 {
-    const int rows_per_group = kRowBlock * MB;
-    dim3 grid(a.T, (a.B + rows_per_group - 1) / rows_per_group);
+    const int rpg = kRowBlock * MB;
+    dim3 grid(((a.T + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg));
     switch (epi) {
     case kEpiPair:
         hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPair>), grid, dim3(kThreads), 0, s, a);
@@ -645,14 +653,9 @@ hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s)
 {
     if (a.B <= 0 || a.T <= 0)
         return hipSuccess;
-    switch (rows_per_group(a.B)) {
-    case kRowBlock:
+    if (rows_per_group(a.B) == kRowBlock)
         return launch_mb<1>(a, epi, s);
-    case 2 * kRowBlock:
-        return launch_mb<2>(a, epi, s);
-    default:
-        return launch_mb<kMaxMB>(a, epi, s);
-    }
+    return launch_mb<kMaxMB>(a, epi, s);
 }
 
 hipError_t launch_combine(const int2 *pair, const float2 *mse, const LaneTable &lanes,

@@ -57,8 +57,8 @@ sb_status check_desc(const sb_head_desc *d)
     }
     if (d->B > kMaxRows)
         return SB_ERR_UNSUPPORTED;
-    // Per-step buffer offsets are 32-bit: 32 hidden rows of a shard and 64
-    // rows of x must span less than 4 GiB.
+    // Per-step buffer offsets are 32-bit: 40 hidden rows of a shard and one
+    // row group of x must span less than 4 GiB.
     if ((int64_t)(sbk::kStepK + 8) * d->ldw * 2 >= ((int64_t)1 << 32) ||
         (int64_t)(sbk::kRowBlock * sbk::kMaxMB) * d->ldx * 2 >= ((int64_t)1 << 32))
         return SB_ERR_UNSUPPORTED;
