@@ -64,6 +64,14 @@ inline int rows_per_group(int B) { return B <= kRowBlock ? kRowBlock : 2 * kRowB
 // through the completion protocol.
 hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s);
 
+// Batches of at least this many rows use the large-batch (MFMA-bound) head
+// GEMM for every surface.
+constexpr int kLargeBatch = 256;
+
+// Large-batch head GEMM: writes the (row, tile) results (and logits /
+// shards) only; ids / lse / sel_lp come from launch_combine afterwards.
+hipError_t launch_head_gemm_large(const HeadArgs &a, int epi, hipStream_t s);
+
 // Fold the (row, tile) workspaces into ids / lse / sel_lp (any may be NULL
 // except ids).  One workgroup per row; tiles folded lane by lane in ascending
 // order, lanes folded in ascending order.

@@ -623,6 +623,302 @@ __global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float *logit
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Large-batch head GEMM (prefill shapes, MFMA-bound).
+//
+// One workgroup = 8 waves = a 256-row x 256-column block of one lane, laid
+// out as 4 (rows) x 2 (columns) waves; each wave owns 64 rows x one
+// 128-column tile, so the per-(row, tile) epilogue results come straight out
+// of one wave.  K advances in 32-row steps through a 3-stage LDS ring filled
+// by direct-to-LDS buffer loads (1 KB per instruction):
+//   * X stage [256 rows][32 k] bf16, 16-byte units XOR-swizzled by row so
+//     that the 16 lanes reading one k-group of 16 rows hit distinct banks;
+//   * W stage [32 k][256 columns] bf16, row-major as in HBM; a lane reads an
+//     8 x 8 block (rows 8g..8g+7, columns 8n..8n+7) and transposes it in
+//     registers with v_perm, as in the decode kernel.
+// Each logit is accumulated over ascending K steps in one wave with
+// v_mfma_f32_16x16x32_bf16.  The token / log-prob / full-logit surfaces all
+// use this mainloop for large batches, so they stay bit-identical.
+// ---------------------------------------------------------------------------
+constexpr int kLBM = 256, kLBN = 256, kLBK = 32;
+constexpr int kLWaves = 8, kLThreads = kLWaves * 64;
+constexpr int kLStages = 3;
+constexpr int kLStageBytes = kLBM * kLBK * 2 + kLBK * kLBN * 2;  // 32 KB
+
+struct LargeGrid {
+    int mblocks;  // ceil(B / 256)
+    int mpx;      // m-blocks per XCD slot (mblocks >= 8) or 0 (plain order)
+    int nblocks;  // total 256-column blocks over all lanes
+};
+
+// Workgroup id -> (m-block, n-block).  With at least 8 m-blocks, XCD slot
+// x = id % 8 (workgroups are handed to the XCDs round-robin) takes m-blocks
+// x, x+8, ... and walks the n-blocks in order, so every XCD keeps its X rows
+// in its own L2 and all XCDs stream the same weight block at about the same
+// time.  With fewer m-blocks the m-blocks of one n-block are consecutive.
+// A placement hint only: any bijection gives the same results.
+__device__ __forceinline__ bool large_block(const LargeGrid &g, int id, int &mb, int &nb)
+{
+    if (g.mpx > 0) {
+        const int xcd = id & 7, local = id >> 3;
+        mb = (local % g.mpx) * 8 + xcd;
+        nb = local / g.mpx;
+    } else {
+        mb = id % g.mblocks;
+        nb = id / g.mblocks;
+    }
+    return mb < g.mblocks && nb < g.nblocks;
+}
+
+__device__ __forceinline__ int nblock_lane(const HeadArgs &a, int nb, int &nb0)
+{
+    // n-blocks of lane i: ceil(V_i / 256), in lane order
+    int lane = 0, first = 0;
+    for (;;) {
+        const int vi = a.lanes.off[lane + 1] - a.lanes.off[lane];
+        const int nbl = (vi + kLBN - 1) / kLBN;
+        if (nb < first + nbl || lane + 1 >= a.lanes.k)
+            break;
+        first += nbl;
+        ++lane;
+    }
+    nb0 = first;
+    return lane;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const HeadArgs a,
+                                                                       const LargeGrid grid)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    int mb, nb;
+    if (!large_block(grid, blockIdx.x, mb, nb))
+        return;
+    int nb0;
+    const int lane = nblock_lane(a, nb, nb0);
+    const int Vi = a.lanes.off[lane + 1] - a.lanes.off[lane];
+    const int c0 = (nb - nb0) * kLBN;  // first column of the block inside the lane
+    const int m0 = mb * kLBM;
+    const int H = a.H;
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int L = threadIdx.x & 63, n = L & 15, g = L >> 4;
+    const int wr = wave >> 1, wc = wave & 1;  // wave row (64 rows), wave column (128 cols)
+
+    // global extents (bytes) from the block origin
+    const uint16_t *wbase = a.lanes.w[lane] + c0;
+    const int64_t wcols = ((int64_t)(Vi - c0) + 7) & ~(int64_t)7;
+    const int64_t wbytes = H > 0 ? (((int64_t)(H - 1) * a.ldw) + wcols) * 2 : 0;
+    const int rows_here = min(a.B - m0, kLBM);
+    const uint16_t *xbase = a.x + (int64_t)m0 * a.ldx;
+    const int64_t xbytes = H > 0 ? (((int64_t)(rows_here - 1) * a.ldx) + ((H + 7) & ~7)) * 2 : 0;
+
+    // DMA work of this wave per stage: X instructions 2*wave, 2*wave+1 (16
+    // rows each), W instructions 2*wave, 2*wave+1 (2 rows each)
+    uint32_t xvo[2], wvo[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int j = 2 * wave + i;       // X instruction: rows 16j .. 16j+15
+        const int r = L >> 2;             // row inside the instruction
+        const int q = (L & 3) ^ ((r >> 2) & 3);  // swizzled 16-byte piece
+        xvo[i] = (uint32_t)((((int64_t)(16 * j + r)) * a.ldx + 8 * q) * 2);
+        const int wrow = 2 * j + (L >> 5);  // W instruction: rows 2j, 2j+1
+        wvo[i] = (uint32_t)((((int64_t)wrow) * a.ldw + 8 * (L & 31)) * 2);
+    }
+    const int nsteps = (H + kLBK - 1) / kLBK;
+    auto issue = [&](int st) {
+        uint8_t *stage = smem + (st % kLStages) * kLStageBytes;
+        const int k0 = st * kLBK;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + k0, xbytes - (int64_t)k0 * 2);
+        const int64_t wshift = (int64_t)k0 * a.ldw;
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + wshift, wbytes - wshift * 2);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int j = 2 * wave + i;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void *)(stage + j * 1024), 16, xvo[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (__attribute__((address_space(3))) void *)(stage + kLBM * kLBK * 2 + j * 1024), 16,
+                wvo[i], 0, 0, 0);
+        }
+    };
+
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            acc[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int j = 0; j < kLStages - 1; ++j)
+        if (j < nsteps)
+            issue(j);
+    for (int st = 0; st < nsteps; ++st) {
+        // this wave's loads for stage st are done once at most the loads of
+        // the younger stages (4 per stage) are outstanding
+        const int younger = min(kLStages - 2, nsteps - 1 - st);
+        if (younger >= 1)
+            __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+        else
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        __builtin_amdgcn_s_barrier();            // every wave's loads are done
+        if (st + kLStages - 1 < nsteps)
+            issue(st + kLStages - 1);            // refills the stage read last step
+        const uint8_t *stage = smem + (st % kLStages) * kLStageBytes;
+        const int k0 = st * kLBK;
+        u32x4 af[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            const int row = wr * 64 + rb * 16 + n;
+            const int j = row >> 4, r = row & 15;
+            af[rb] = *reinterpret_cast<const u32x4 *>(stage + j * 1024 + (r * 4 + (g ^ ((r >> 2) & 3))) * 16);
+        }
+        if (k0 + kLBK > H) {
+            const int h0 = k0 + 8 * g;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    uint32_t v = af[rb][d];
+                    if (h0 + 2 * d >= H)
+                        v &= 0xFFFF0000u;
+                    if (h0 + 2 * d + 1 >= H)
+                        v &= 0x0000FFFFu;
+                    af[rb][d] = v;
+                }
+        }
+        u32x4 wq[8];
+        const uint8_t *wst = stage + kLBM * kLBK * 2;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            wq[r] = *reinterpret_cast<const u32x4 *>(wst + (8 * g + r) * (kLBN * 2) + (wc * 128 + 8 * n) * 2);
+        bf16x8 xa[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            xa[rb] = __builtin_bit_cast(bf16x8, af[rb]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            u32x4 bq;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                bq[q] = __builtin_amdgcn_perm(wq[2 * q + 1][c >> 1], wq[2 * q][c >> 1], sel);
+            const bf16x8 bb = __builtin_bit_cast(bf16x8, bq);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                acc[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[rb], bb, acc[rb][c], 0, 0, 0);
+        }
+    }
+
+    // ---------------- epilogue: this wave's 64 rows x 128-column tile ----------------
+    const int tc0 = c0 + wc * 128;                 // tile's first column inside the lane
+    if (tc0 >= Vi)
+        return;                                    // past the lane's last tile
+    const int tile = a.lanes.tile0[lane] + tc0 / kTileN;
+    const int colrel = tc0 + 8 * n;                // this lane's first column inside the lane
+    const int nvalid = max(0, min(8, Vi - colrel));
+    const int gcol = a.lanes.off[lane] + colrel;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int b = m0 + wr * 64 + rb * 16 + 4 * g + r;
+            const bool rowok = b < a.B;
+            float y[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                y[c] = acc[rb][c][r];
+            if (EPI == kEpiShard || EPI == kEpiPairLseOut) {
+                float *dst = EPI == kEpiShard
+                                 ? a.lanes.shard[lane] + (int64_t)b * a.lanes.shard_ld[lane] + colrel
+                                 : a.out + (int64_t)b * a.ldo + gcol;
+                if (rowok) {
+                    if (nvalid == 8 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                        *reinterpret_cast<f32x4 *>(dst) = f32x4{y[0], y[1], y[2], y[3]};
+                        *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{y[4], y[5], y[6], y[7]};
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 8; ++c)
+                            if (c < nvalid)
+                                dst[c] = y[c];
+                    }
+                }
+            }
+            if (EPI != kEpiShard) {
+                float bv = -INFINITY;
+                int bi = INT_MAX;
+                if (nvalid > 0) {
+                    bv = y[0];
+                    bi = gcol;
+                }
+#pragma unroll
+                for (int c = 1; c < 8; ++c)
+                    if (c < nvalid && y[c] > bv) {
+                        bv = y[c];
+                        bi = gcol + c;
+                    }
+#pragma unroll
+                for (int o = 8; o >= 1; o >>= 1) {
+                    const float ov = __shfl_xor(bv, o, 16);
+                    const int oi = __shfl_xor(bi, o, 16);
+                    if (better(ov, oi, bv, bi)) {
+                        bv = ov;
+                        bi = oi;
+                    }
+                }
+                float se = 0.f;
+                if (EPI != kEpiPair) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c)
+                        if (c < nvalid)
+                            se += __expf(y[c] - bv);
+#pragma unroll
+                    for (int o = 8; o >= 1; o >>= 1)
+                        se += __shfl_xor(se, o, 16);
+                }
+                if (n == 0 && rowok) {
+                    const int64_t idx = (int64_t)b * a.T + tile;
+                    a.pair[idx] = make_int2(__float_as_int(bv), bi);
+                    if (EPI != kEpiPair)
+                        a.mse[idx] = make_float2(bv, se);
+                }
+            }
+        }
+    }
+}
+
+template <int EPI>
+hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
+{
+    LargeGrid g;
+    g.mblocks = (a.B + kLBM - 1) / kLBM;
+    g.nblocks = 0;
+    for (int i = 0; i < a.lanes.k; ++i)
+        g.nblocks += (a.lanes.off[i + 1] - a.lanes.off[i] + kLBN - 1) / kLBN;
+    int64_t nwg;
+    if (g.mblocks >= 8) {
+        g.mpx = (g.mblocks + 7) / 8;
+        nwg = (int64_t)8 * g.mpx * g.nblocks;
+    } else {
+        g.mpx = 0;
+        nwg = (int64_t)g.mblocks * g.nblocks;
+    }
+    const size_t lds = (size_t)kLStages * kLStageBytes;
+    static bool attr_set = false;  // idempotent; a race only repeats the call
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)head_gemm_large_kernel<EPI>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(head_gemm_large_kernel<EPI>, dim3((unsigned)nwg), dim3(kLThreads), lds, s,
+                       a, g);
+    return hipGetLastError();
+}
+
 template <int MB>
 hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
 {
@@ -656,6 +952,24 @@ hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s)
     if (rows_per_group(a.B) == kRowBlock)
         return launch_mb<1>(a, epi, s);
     return launch_mb<kMaxMB>(a, epi, s);
+}
+
+hipError_t launch_head_gemm_large(const HeadArgs &a, int epi, hipStream_t s)
+{
+    if (a.B <= 0 || a.T <= 0)
+        return hipSuccess;
+    switch (epi) {
+    case kEpiPair:
+        return launch_large_epi<kEpiPair>(a, s);
+    case kEpiPairLse:
+        return launch_large_epi<kEpiPairLse>(a, s);
+    case kEpiPairLseOut:
+        return launch_large_epi<kEpiPairLseOut>(a, s);
+    case kEpiShard:
+        return launch_large_epi<kEpiShard>(a, s);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_combine(const int2 *pair, const float2 *mse, const LaneTable &lanes,

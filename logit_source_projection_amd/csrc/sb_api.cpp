@@ -221,6 +221,13 @@ sb_status sb_project_tokens(const sb_head_desc *desc, int32_t *ids, void *ws, si
     a.pair = region<int2>(ws, L.pair);
     a.lane_pair = region<int2>(ws, L.lane_pair);
     a.ids = ids;
+    if (a.B >= sbk::kLargeBatch) {
+        if (sbk::launch_head_gemm_large(a, sbk::kEpiPair, s) != hipSuccess ||
+            sbk::launch_combine(a.pair, nullptr, a.lanes, a.B, a.T, ids, nullptr, nullptr, s) !=
+                hipSuccess)
+            return SB_ERR_HIP;
+        return SB_OK;
+    }
     if (sbk::launch_head_gemm(a, sbk::kEpiPair, s) != hipSuccess)
         return SB_ERR_HIP;
     return SB_OK;
@@ -259,9 +266,15 @@ sb_status sb_project_logprobs(const sb_head_desc *desc, int32_t *ids, float *lse
     a.sel_lp = sel_lp;
     a.out = logprobs;
     a.ldo = ldlp;
-    if (sbk::launch_head_gemm(a, logprobs ? sbk::kEpiPairLseOut : sbk::kEpiPairLse, s) !=
-        hipSuccess)
+    const int epi = logprobs ? sbk::kEpiPairLseOut : sbk::kEpiPairLse;
+    if (a.B >= sbk::kLargeBatch) {
+        if (sbk::launch_head_gemm_large(a, epi, s) != hipSuccess ||
+            sbk::launch_combine(a.pair, a.mse, a.lanes, a.B, a.T, ids, lse, sel_lp, s) !=
+                hipSuccess)
+            return SB_ERR_HIP;
+    } else if (sbk::launch_head_gemm(a, epi, s) != hipSuccess) {
         return SB_ERR_HIP;
+    }
     if (logprobs && sbk::launch_normalize(logprobs, ldlp, lse, a.B, a.V, s) != hipSuccess)
         return SB_ERR_HIP;
     return SB_OK;
@@ -291,7 +304,9 @@ sb_status sb_full_logits(const sb_head_desc *desc, float *logits, int64_t ldl, i
         a.lanes.shard[i] = region<float>(ws, L.shard[i]);
         a.lanes.shard_ld[i] = shard_ld(lane_width(desc, i));
     }
-    if (sbk::launch_head_gemm(a, sbk::kEpiShard, s) != hipSuccess)
+    const hipError_t e = a.B >= sbk::kLargeBatch ? sbk::launch_head_gemm_large(a, sbk::kEpiShard, s)
+                                                  : sbk::launch_head_gemm(a, sbk::kEpiShard, s);
+    if (e != hipSuccess)
         return SB_ERR_HIP;
     if (sbk::launch_reconstruct(a.lanes, a.B, logits, ldl, s) != hipSuccess)
         return SB_ERR_HIP;

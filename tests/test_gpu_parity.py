@@ -52,6 +52,11 @@ SMALL = [
     (130, 72, 1536, [0, 512, 1024, 1536], False),
     (5, 8, 100, [0, 50, 100], True),
     (3, 40, 129, [0, 129], True),
+    # large-batch kernel (256-row x 256-column blocks)
+    (256, 96, 1536, [0, 512, 1024, 1536], False),
+    (300, 200, 3000, [0, 1000, 1001, 2999, 3000], True),
+    (513, 72, 777, [0, 300, 777], True),
+    (2100, 40, 520, [0, 256, 520], False),
 ]
 
 
@@ -61,8 +66,9 @@ def test_small_heads(require_gpu, B, H, V, off, sep):
     _case(d, lanes_separate=sep)
 
 
-def test_non_finite_padding_is_never_read(require_gpu):
-    B, H, V = 9, 100, 700
+@pytest.mark.parametrize("B", [9, 260])
+def test_non_finite_padding_is_never_read(require_gpu, B):
+    H, V = 100, 700
     off = [0, 200, 433, 700]
     d = inputs.make_random(B, H, V, off, seed=5)
     g, _, _ = _case(d, lanes_separate=True, pad_w=24, pad_x=28)
@@ -134,8 +140,9 @@ def test_exact_ties_across_and_within_lanes(require_gpu):
     assert list(g["ids_tok"][[0, 2, 3]]) == [700, 1030, 1023]
 
 
-def test_lane_count_invariance(require_gpu):
-    B, H, V = 16, 1024, 8192
+@pytest.mark.parametrize("B", [16, 300])
+def test_lane_count_invariance(require_gpu, B):
+    H, V = 1024, 8192
     d = inputs.make_random(B, H, V, [0, V], seed=12)
     outs = []
     for k in (1, 2, 4, 8):
