@@ -641,10 +641,28 @@ __global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float *logit
 // v_mfma_f32_16x16x32_bf16.  The token / log-prob / full-logit surfaces all
 // use this mainloop for large batches, so they stay bit-identical.
 // ---------------------------------------------------------------------------
-constexpr int kLBM = 256, kLBN = 256, kLBK = 32;
+constexpr int kLBM = 256, kLBN = 256, kLBK = 64;
 constexpr int kLWaves = 8, kLThreads = kLWaves * 64;
-constexpr int kLStages = 3;
-constexpr int kLStageBytes = kLBM * kLBK * 2 + kLBK * kLBN * 2;  // 32 KB
+constexpr int kLStages = 2;                     // LDS ring depth (X and W stages)
+constexpr int kLStageXBytes = kLBM * kLBK * 2;  // 32 KB at BK = 64
+constexpr int kLStageWBytes = kLBK * kLBN * 2;  // 32 KB at BK = 64
+constexpr int kLLdsBytes = kLStages * (kLStageXBytes + kLStageWBytes);
+constexpr int kLSub = kLBK / 32;          // 32-deep MFMA steps per stage
+constexpr int kLPieces = kLBK * 2 / 16;   // 16-byte pieces per X row in a stage
+constexpr int kLRowsPerInst = 64 / kLPieces;                  // X rows per 1 KB load
+constexpr int kLXInst = kLBM / kLRowsPerInst / kLWaves;       // X loads per wave per stage
+constexpr int kLWInst = kLBK / 2 / kLWaves;                   // W loads per wave per stage
+static_assert(kLBK == 32 || kLBK == 64, "X swizzle is defined for 4 or 8 pieces per row");
+static_assert(kLLdsBytes <= 160 * 1024, "LDS rings must fit in 160 KB");
+static_assert(kLStages == 2, "the wait counts below assume a two-stage ring");
+
+// X stage layout: 1 KB load j holds rows j*R .. j*R+R-1 (R = kLRowsPerInst);
+// the 16-byte piece q of row r sits in slot q ^ swz(r, j).  The swizzle
+// spreads the 16 rows a fragment read touches over distinct LDS banks.
+__device__ __forceinline__ int x_swz(int r, int j)
+{
+    return kLPieces == 4 ? ((r >> 2) & 3) : (((r >> 1) & 3) | ((j & 1) << 2));
+}
 
 struct LargeGrid {
     int mblocks;  // ceil(B / 256)
@@ -714,34 +732,44 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     const uint16_t *xbase = a.x + (int64_t)m0 * a.ldx;
     const int64_t xbytes = H > 0 ? (((int64_t)(rows_here - 1) * a.ldx) + ((H + 7) & ~7)) * 2 : 0;
 
-    // DMA work of this wave per stage: X instructions 2*wave, 2*wave+1 (16
-    // rows each), W instructions 2*wave, 2*wave+1 (2 rows each)
-    uint32_t xvo[2], wvo[2];
+    // this wave's loads per stage: X loads kLXInst*wave .. (kLRowsPerInst rows
+    // each) and W loads kLWInst*wave .. (2 rows of 512 B each)
+    uint32_t xvo[kLXInst], wvo[kLWInst];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int j = 2 * wave + i;       // X instruction: rows 16j .. 16j+15
-        const int r = L >> 2;             // row inside the instruction
-        const int q = (L & 3) ^ ((r >> 2) & 3);  // swizzled 16-byte piece
-        xvo[i] = (uint32_t)((((int64_t)(16 * j + r)) * a.ldx + 8 * q) * 2);
-        const int wrow = 2 * j + (L >> 5);  // W instruction: rows 2j, 2j+1
+    for (int i = 0; i < kLXInst; ++i) {
+        const int j = kLXInst * wave + i;
+        const int r = L / kLPieces;
+        const int q = (L % kLPieces) ^ x_swz(r, j);
+        xvo[i] = (uint32_t)((((int64_t)(kLRowsPerInst * j + r)) * a.ldx + 8 * q) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < kLWInst; ++i) {
+        const int j = kLWInst * wave + i;
+        const int wrow = 2 * j + (L >> 5);
         wvo[i] = (uint32_t)((((int64_t)wrow) * a.ldw + 8 * (L & 31)) * 2);
     }
     const int nsteps = (H + kLBK - 1) / kLBK;
-    auto issue = [&](int st) {
-        uint8_t *stage = smem + (st % kLStages) * kLStageBytes;
+    uint8_t *const xring = smem;
+    uint8_t *const wring = smem + kLStages * kLStageXBytes;
+    auto issue_x = [&](int st) {
+        uint8_t *stage = xring + (st % kLStages) * kLStageXBytes;
         const int k0 = st * kLBK;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + k0, xbytes - (int64_t)k0 * 2);
-        const int64_t wshift = (int64_t)k0 * a.ldw;
+#pragma unroll
+        for (int i = 0; i < kLXInst; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void *)(stage + (kLXInst * wave + i) * 1024),
+                16, xvo[i], 0, 0, 0);
+    };
+    auto issue_w = [&](int st) {
+        uint8_t *stage = wring + (st % kLStages) * kLStageWBytes;
+        const int64_t wshift = (int64_t)st * kLBK * a.ldw;
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + wshift, wbytes - wshift * 2);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int j = 2 * wave + i;
+        for (int i = 0; i < kLWInst; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (__attribute__((address_space(3))) void *)(stage + j * 1024), 16, xvo[i], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (__attribute__((address_space(3))) void *)(stage + kLBM * kLBK * 2 + j * 1024), 16,
-                wvo[i], 0, 0, 0);
-        }
+                rw, (__attribute__((address_space(3))) void *)(stage + (kLWInst * wave + i) * 1024),
+                16, wvo[i], 0, 0, 0);
     };
 
     f32x4 acc[4][8];
@@ -751,64 +779,69 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
         for (int c = 0; c < 8; ++c)
             acc[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-    for (int j = 0; j < kLStages - 1; ++j)
-        if (j < nsteps)
-            issue(j);
+    // Two-stage ring: step st+1 is loaded while step st is computed.
+    if (nsteps > 0) {
+        issue_x(0);
+        issue_w(0);
+    }
     for (int st = 0; st < nsteps; ++st) {
-        // this wave's loads for stage st are done once at most the loads of
-        // the younger stages (4 per stage) are outstanding
-        const int younger = min(kLStages - 2, nsteps - 1 - st);
-        if (younger >= 1)
-            __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
-        else
-            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-        __builtin_amdgcn_s_barrier();            // every wave's loads are done
-        if (st + kLStages - 1 < nsteps)
-            issue(st + kLStages - 1);            // refills the stage read last step
-        const uint8_t *stage = smem + (st % kLStages) * kLStageBytes;
-        const int k0 = st * kLBK;
-        u32x4 af[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int row = wr * 64 + rb * 16 + n;
-            const int j = row >> 4, r = row & 15;
-            af[rb] = *reinterpret_cast<const u32x4 *>(stage + j * 1024 + (r * 4 + (g ^ ((r >> 2) & 3))) * 16);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of step st
+        __builtin_amdgcn_s_barrier();        // every wave's loads are in LDS and
+                                             // every wave is done reading step st-1
+        if (st + 1 < nsteps) {
+            issue_x(st + 1);                 // refills the slots of step st-1
+            issue_w(st + 1);
         }
-        if (k0 + kLBK > H) {
-            const int h0 = k0 + 8 * g;
+        const uint8_t *stage = xring + (st % kLStages) * kLStageXBytes;
+        const uint8_t *wst = wring + (st % kLStages) * kLStageWBytes;
+#pragma unroll
+        for (int ks = 0; ks < kLSub; ++ks) {
+            const int k0 = st * kLBK + 32 * ks;
+            u32x4 af[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int row = wr * 64 + rb * 16 + n;
+                const int j = row / kLRowsPerInst, r = row % kLRowsPerInst;
+                const int piece = 4 * ks + g;
+                af[rb] = *reinterpret_cast<const u32x4 *>(
+                    stage + j * 1024 + (r * kLPieces + (piece ^ x_swz(r, j))) * 16);
+            }
+            if (k0 + 32 > H) {
+                const int h0 = k0 + 8 * g;
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        uint32_t v = af[rb][d];
+                        if (h0 + 2 * d >= H)
+                            v &= 0xFFFF0000u;
+                        if (h0 + 2 * d + 1 >= H)
+                            v &= 0x0000FFFFu;
+                        af[rb][d] = v;
+                    }
+            }
+            u32x4 wq[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                wq[r] = *reinterpret_cast<const u32x4 *>(wst + (32 * ks + 8 * g + r) * (kLBN * 2) +
+                                                         (wc * 128 + 8 * n) * 2);
+            bf16x8 xa[4];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
+                xa[rb] = __builtin_bit_cast(bf16x8, af[rb]);
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    uint32_t v = af[rb][d];
-                    if (h0 + 2 * d >= H)
-                        v &= 0xFFFF0000u;
-                    if (h0 + 2 * d + 1 >= H)
-                        v &= 0x0000FFFFu;
-                    af[rb][d] = v;
-                }
-        }
-        u32x4 wq[8];
-        const uint8_t *wst = stage + kLBM * kLBK * 2;
+            for (int c = 0; c < 8; ++c) {
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                u32x4 bq;
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            wq[r] = *reinterpret_cast<const u32x4 *>(wst + (8 * g + r) * (kLBN * 2) + (wc * 128 + 8 * n) * 2);
-        bf16x8 xa[4];
+                for (int q = 0; q < 4; ++q)
+                    bq[q] = __builtin_amdgcn_perm(wq[2 * q + 1][c >> 1], wq[2 * q][c >> 1], sel);
+                const bf16x8 bb = __builtin_bit_cast(bf16x8, bq);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            xa[rb] = __builtin_bit_cast(bf16x8, af[rb]);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-            u32x4 bq;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                bq[q] = __builtin_amdgcn_perm(wq[2 * q + 1][c >> 1], wq[2 * q][c >> 1], sel);
-            const bf16x8 bb = __builtin_bit_cast(bf16x8, bq);
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-                acc[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[rb], bb, acc[rb][c], 0, 0, 0);
+                for (int rb = 0; rb < 4; ++rb)
+                    acc[rb][c] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[rb], bb, acc[rb][c], 0, 0, 0);
+            }
         }
     }
 
@@ -905,7 +938,7 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
         g.mpx = 0;
         nwg = (int64_t)g.mblocks * g.nblocks;
     }
-    const size_t lds = (size_t)kLStages * kLStageBytes;
+    const size_t lds = (size_t)kLLdsBytes;
     static bool attr_set = false;  // idempotent; a race only repeats the call
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)head_gemm_large_kernel<EPI>,
