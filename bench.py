@@ -37,6 +37,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-report", action="store_true",
                     help="skip the extra surfaces timed for the report")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the timed "
+                         "region (reference kernel for HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: read two rocprofv3 --pmc counter_collection.csv "
+                         "files (FETCH_SIZE, WRITE_SIZE) of a run made with "
+                         "--copy-calibration-mib, and record the head kernel's HBM bytes "
+                         "per launch for --workload/--surface/--B")
     return ap.parse_args()
 
 
@@ -56,6 +64,100 @@ def algorithmic_bytes(d, surface):
 
 def flops(d):
     return 2 * d["B"] * d["H"] * d["V"]
+
+
+KERNEL_SOURCES = ("logit_source_projection_amd/csrc/kernels.hip",
+                  "logit_source_projection_amd/csrc/kernels.h",
+                  "logit_source_projection_amd/csrc/sb_api.cpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, surface, B):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none for this workload or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    e = rec.get("workloads", {}).get(f"{workload}/{surface}/B{B}")
+    if not e:
+        return None
+    return e["fetch_bytes"] + e["write_bytes"]
+
+
+def _counter_per_dispatch(csv_path):
+    """{kernel name: [counter KiB summed over instances, one per dispatch]}."""
+    import collections
+    import csv
+    per = collections.defaultdict(float)
+    names = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    out = collections.defaultdict(list)
+    for disp, v in per.items():
+        out[names[disp]].append(v)
+    return out
+
+
+def record_traffic(args):
+    """Scale the head kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by
+    what the same counters read for the plain copy of known size run in the
+    same process, and store the bytes per launch in the traffic file."""
+    from logit_source_projection_amd import inputs
+    calib = args.copy_calibration_mib << 20
+    if calib <= 0:
+        sys.exit("--record-traffic needs the --copy-calibration-mib of the profiled run")
+    rec = {}
+    for which, path in zip(("fetch", "write"), args.record_traffic):
+        per = _counter_per_dispatch(path)
+        copy = [v for k, vs in per.items() if "copyBuffer" in k for v in vs]
+        heads = {k: vs for k, vs in per.items() if "head_gemm" in k}
+        if len(copy) != 1 or not heads:
+            sys.exit(f"{path}: expected one copy dispatch and head kernel dispatches")
+        name, vals = max(heads.items(), key=lambda kv: len(kv[1]))
+        factor = calib / (copy[0] * 1024.0)
+        kib = sum(vals) / len(vals)
+        rec[which] = dict(kernel=name, dispatches=len(vals), kib_per_dispatch=round(kib, 3),
+                          copy_kib=copy[0], factor=round(factor, 5),
+                          bytes=int(round(kib * 1024.0 * factor)))
+    if rec["fetch"]["kernel"] != rec["write"]["kernel"]:
+        sys.exit("the two passes name different head kernels")
+    d = inputs.WORKLOADS[args.workload]
+    B = args.B if args.B is not None else d[0]
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    sha = kernel_source_hash()
+    if data.get("kernel_source_sha256") != sha:
+        data = {"kernel_source_sha256": sha, "workloads": {}}
+    data["calibration"] = (f"one device copy of {args.copy_calibration_mib} MiB in the same "
+                           "process; factor = copy bytes / counter bytes of that copy")
+    data["workloads"][f"{args.workload}/{args.surface}/B{B}"] = dict(
+        kernel=rec["fetch"]["kernel"], fetch_bytes=rec["fetch"]["bytes"],
+        write_bytes=rec["write"]["bytes"],
+        fetch_kib_per_dispatch=rec["fetch"]["kib_per_dispatch"],
+        write_kib_per_dispatch=rec["write"]["kib_per_dispatch"],
+        fetch_factor=rec["fetch"]["factor"], write_factor=rec["write"]["factor"],
+        dispatches=rec["fetch"]["dispatches"])
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(data["workloads"][f"{args.workload}/{args.surface}/B{B}"]))
 
 
 def result_cut_percent(bytes_projected, bytes_full):
@@ -150,6 +252,9 @@ def cpu_baseline(d):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -167,6 +272,14 @@ def main():
     with torch.cuda.stream(stream):
         run = Runner(d, stream)
     torch.cuda.synchronize()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # warmup, then exactly `steps` timed steps
     for _ in range(args.warmup):
@@ -179,9 +292,12 @@ def main():
     rows_s = B / (ms * 1e-3)
     nbytes = algorithmic_bytes(d, args.surface)
     achieved = nbytes / (ms * 1e-3) / 1e9
+    one_launch = B < 256 and args.surface in ("tokens", "logprobs")
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel="head GEMM + fused epilogue (whole call)",
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=recorded_traffic(args.workload, args.surface, B),
+                    kernel=("head_gemm_kernel (the whole call is this one launch)" if one_launch
+                            else "whole call (head GEMM and its follow-up kernels)"),
                     algorithmic_bytes=nbytes)
     if args.workload == "prefill":
         tf = flops(d) / (ms * 1e-3) / 1e12

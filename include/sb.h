@@ -29,6 +29,11 @@
  *    each logit is accumulated depends only on (B, H), never on the surface,
  *    the lane split or the column position, so the three calls return
  *    bit-identical logits and IDs for the same inputs.
+ *  - lse is an online sum over 128-column tiles.  A lane's tile grid starts on
+ *    the cache line that holds the lane's first column, so lse (and sel_lp and
+ *    the complete log-probs) can differ in the last bits between shard
+ *    placements that differ modulo 128 bytes; for the same placement it is
+ *    reproduced exactly.
  *  - Inputs must be finite with |logit| < FLT_MAX; behaviour on NaN/Inf input
  *    is unspecified.
  *

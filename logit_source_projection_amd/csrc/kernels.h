@@ -13,6 +13,10 @@ constexpr int kWaves = 4;       // waves per workgroup; K steps interleaved over
 constexpr int kRowBlock = 16;   // rows per MFMA row block
 constexpr int kMaxMB = 2;       // row blocks per workgroup
 constexpr int kArgmaxChunk = 8192;  // columns per workgroup in the full-logit argmax
+constexpr int kLineBytes = 128;     // L2 cache line
+// A lane's tile grid starts up to this many columns before its first column,
+// so that tiles begin on a cache line (shard bases are 16-byte aligned).
+constexpr int kMaxShift = (kLineBytes - 16) / 2;
 
 // Epilogue variants of the head GEMM.
 enum Epilogue : int {
@@ -28,6 +32,12 @@ struct LaneTable {
     float *shard[kMaxLanes];       // lane i's fp32 shard (kEpiShard)
     int32_t off[kMaxLanes + 1];    // vocab offsets
     int32_t tile0[kMaxLanes + 1];  // first tile of lane i (prefix sums)
+    // Tile t of lane i covers lane columns [t*kTileN - shift[i], +kTileN):
+    // shift[i] (a multiple of 8, at most kMaxShift) puts every tile but the
+    // first on a cache-line boundary, so that neighbouring tiles, which run
+    // on different XCDs, never fetch the same line.  Columns before the
+    // lane's first are loaded from column 0 and dropped.
+    int32_t shift[kMaxLanes];
     int32_t shard_ld[kMaxLanes];   // row stride of lane i's shard
     int32_t k;
 };
@@ -38,7 +48,7 @@ struct HeadArgs {
     int64_t ldx;
     int64_t ldw;
     int32_t B, H, V;
-    int32_t T;           // total tiles (row stride of the pair workspaces)
+    int32_t T;           // row stride of the pair workspaces (>= lanes.tile0[k])
     int2 *pair;          // [B][T] {float bits of max, global index}
     float2 *mse;         // [B][T] {tile max, sum exp(y - tile max)}
     float *out;          // [B][ldo] fp32 logits at global columns (kEpiPairLseOut)
@@ -53,6 +63,9 @@ struct HeadArgs {
     float *lse;          // [B] or null
     float *sel_lp;       // [B] or null
 };
+
+// Tiles of a lane of vi columns whose grid starts `shift` columns early.
+inline int lane_tiles(int vi, int shift) { return (vi + shift + kTileN - 1) / kTileN; }
 
 // Rows per workgroup row group for a batch of B rows: one 16-row MFMA block
 // up to 16 rows, two above (more rows run as further row groups, dispatched

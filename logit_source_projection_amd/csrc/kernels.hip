@@ -293,10 +293,12 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
     const int q = blockIdx.x >> 3;
     const int tile = (q / groups) * 8 + (blockIdx.x & 7);
     const int group = q - (q / groups) * groups;
-    if (tile >= a.T)
+    if (tile >= a.lanes.tile0[a.lanes.k])
         return;
     const int lane = find_lane(a.lanes, tile);
-    const int c0 = (tile - a.lanes.tile0[lane]) * kTileN;  // first column inside the lane
+    // first column inside the lane (negative in a shifted lane's first tile)
+    const int c0 = (tile - a.lanes.tile0[lane]) * kTileN - a.lanes.shift[lane];
+    const int cb = max(c0, 0);                              // first column loaded
     const int Vi = a.lanes.off[lane + 1] - a.lanes.off[lane];
     const int gcol0 = a.lanes.off[lane] + c0;               // first global column
     const int m0 = group * (kRowBlock * MB);
@@ -308,10 +310,10 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
     const int g = L >> 4;
     const int H = a.H;
 
-    // Readable extents (bytes) from the tile's origin: through the last valid
-    // column of the last hidden row, rounded up to whole 16-byte vectors.
-    const uint16_t *wbase = a.lanes.w[lane] + c0;
-    const int64_t wcols = ((int64_t)(Vi - c0) + 7) & ~(int64_t)7;
+    // Readable extents (bytes) from the first loaded column: through the last
+    // valid column of the last hidden row, rounded up to whole 16-byte vectors.
+    const uint16_t *wbase = a.lanes.w[lane] + cb;
+    const int64_t wcols = ((int64_t)(Vi - cb) + 7) & ~(int64_t)7;
     const int64_t wbytes = H > 0 ? (((int64_t)(H - 1) * a.ldw) + wcols) * 2 : 0;
     const int rows_here = min(a.B - m0, kRowBlock * MB);
     const uint16_t *xbase = a.x + (int64_t)m0 * a.ldx;
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
     uint32_t wvo[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-        wvo[r] = (uint32_t)(((int64_t)(8 * g + r) * a.ldw + 8 * n) * 2);
+        wvo[r] = (uint32_t)(((int64_t)(8 * g + r) * a.ldw + max(c0 + 8 * n - cb, 0)) * 2);
     uint32_t xvo[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
     const int erow = threadIdx.x >> 4;  // 0..15: row inside the block
     const int cg = threadIdx.x & 15;    // 8-column group inside the tile
     const int colrel = c0 + 8 * cg;     // column inside the lane
-    const int nvalid = max(0, min(8, Vi - colrel));
+    const int nvalid = colrel < 0 ? 0 : max(0, min(8, Vi - colrel));
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         if (m0 + kRowBlock * mb >= a.B)
@@ -691,11 +693,11 @@ __device__ __forceinline__ bool large_block(const LargeGrid &g, int id, int &mb,
 
 __device__ __forceinline__ int nblock_lane(const HeadArgs &a, int nb, int &nb0)
 {
-    // n-blocks of lane i: ceil(V_i / 256), in lane order
+    // n-blocks of lane i: ceil((V_i + shift_i) / 256), in lane order
     int lane = 0, first = 0;
     for (;;) {
         const int vi = a.lanes.off[lane + 1] - a.lanes.off[lane];
-        const int nbl = (vi + kLBN - 1) / kLBN;
+        const int nbl = (vi + a.lanes.shift[lane] + kLBN - 1) / kLBN;
         if (nb < first + nbl || lane + 1 >= a.lanes.k)
             break;
         first += nbl;
@@ -716,7 +718,10 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     int nb0;
     const int lane = nblock_lane(a, nb, nb0);
     const int Vi = a.lanes.off[lane + 1] - a.lanes.off[lane];
-    const int c0 = (nb - nb0) * kLBN;  // first column of the block inside the lane
+    // first column of the block inside the lane (negative in a shifted
+    // lane's first block) and the first column loaded
+    const int c0 = (nb - nb0) * kLBN - a.lanes.shift[lane];
+    const int cb = max(c0, 0);
     const int m0 = mb * kLBM;
     const int H = a.H;
 
@@ -724,9 +729,9 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     const int L = threadIdx.x & 63, n = L & 15, g = L >> 4;
     const int wr = wave >> 1, wc = wave & 1;  // wave row (64 rows), wave column (128 cols)
 
-    // global extents (bytes) from the block origin
-    const uint16_t *wbase = a.lanes.w[lane] + c0;
-    const int64_t wcols = ((int64_t)(Vi - c0) + 7) & ~(int64_t)7;
+    // global extents (bytes) from the first loaded column
+    const uint16_t *wbase = a.lanes.w[lane] + cb;
+    const int64_t wcols = ((int64_t)(Vi - cb) + 7) & ~(int64_t)7;
     const int64_t wbytes = H > 0 ? (((int64_t)(H - 1) * a.ldw) + wcols) * 2 : 0;
     const int rows_here = min(a.B - m0, kLBM);
     const uint16_t *xbase = a.x + (int64_t)m0 * a.ldx;
@@ -746,7 +751,7 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     for (int i = 0; i < kLWInst; ++i) {
         const int j = kLWInst * wave + i;
         const int wrow = 2 * j + (L >> 5);
-        wvo[i] = (uint32_t)((((int64_t)wrow) * a.ldw + 8 * (L & 31)) * 2);
+        wvo[i] = (uint32_t)((((int64_t)wrow) * a.ldw + max(c0 + 8 * (L & 31) - cb, 0)) * 2);
     }
     const int nsteps = (H + kLBK - 1) / kLBK;
     uint8_t *const xring = smem;
@@ -849,9 +854,9 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     const int tc0 = c0 + wc * 128;                 // tile's first column inside the lane
     if (tc0 >= Vi)
         return;                                    // past the lane's last tile
-    const int tile = a.lanes.tile0[lane] + tc0 / kTileN;
+    const int tile = a.lanes.tile0[lane] + (tc0 + a.lanes.shift[lane]) / kTileN;
     const int colrel = tc0 + 8 * n;                // this lane's first column inside the lane
-    const int nvalid = max(0, min(8, Vi - colrel));
+    const int nvalid = colrel < 0 ? 0 : max(0, min(8, Vi - colrel));
     const int gcol = a.lanes.off[lane] + colrel;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -929,7 +934,7 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
     g.mblocks = (a.B + kLBM - 1) / kLBM;
     g.nblocks = 0;
     for (int i = 0; i < a.lanes.k; ++i)
-        g.nblocks += (a.lanes.off[i + 1] - a.lanes.off[i] + kLBN - 1) / kLBN;
+        g.nblocks += (a.lanes.off[i + 1] - a.lanes.off[i] + a.lanes.shift[i] + kLBN - 1) / kLBN;
     int64_t nwg;
     if (g.mblocks >= 8) {
         g.mpx = (g.mblocks + 7) / 8;
@@ -956,7 +961,8 @@ template <int MB>
 hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
 {
     const int rpg = kRowBlock * MB;
-    dim3 grid(((a.T + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg));
+    const int ntiles = a.lanes.tile0[a.lanes.k];
+    dim3 grid(((ntiles + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg));
     switch (epi) {
     case kEpiPair:
         hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPair>), grid, dim3(kThreads), 0, s, a);

@@ -70,7 +70,7 @@ int lane_width(const sb_head_desc *d, int i) { return d->lane_off[i + 1] - d->la
 int shard_ld(int vi) { return (vi + 3) & ~3; }
 
 struct Layout {
-    int T = 0;            // total tiles
+    int T = 0;            // tile capacity: row stride of the (row, tile) regions
     int nchunks = 0;      // full-logit argmax chunks per row
     int groups = 0;       // row groups (grid y) of the head GEMM
     size_t sync = 0, pair = 0, mse = 0, lane_pair = 0, lane_mse = 0;
@@ -81,8 +81,10 @@ struct Layout {
 Layout layout(const sb_head_desc *d, int surface)
 {
     Layout L;
+    // Sized for the largest tile shift, so that the workspace size does not
+    // depend on where the shards sit in memory.
     for (int i = 0; i < d->k; ++i)
-        L.T += (lane_width(d, i) + sbk::kTileN - 1) / sbk::kTileN;
+        L.T += sbk::lane_tiles(lane_width(d, i), sbk::kMaxShift);
     L.nchunks = (d->V + sbk::kArgmaxChunk - 1) / sbk::kArgmaxChunk;
     const size_t B = (size_t)d->B;
     size_t at = 0;
@@ -138,7 +140,13 @@ void fill_lanes(const sb_head_desc *d, sbk::LaneTable &t)
         t.w[i] = static_cast<const uint16_t *>(d->w[i]);
         t.off[i] = d->lane_off[i];
         t.tile0[i] = tiles;
-        tiles += (lane_width(d, i) + sbk::kTileN - 1) / sbk::kTileN;
+        // columns between the start of the cache line holding the shard's
+        // first column and that column, in whole 16-byte units (at most
+        // kMaxShift; a base that is not 16-byte aligned is only accepted
+        // when nothing is read from it)
+        const uintptr_t line_off = reinterpret_cast<uintptr_t>(d->w[i]) % sbk::kLineBytes;
+        t.shift[i] = (int32_t)(line_off / 16 * 8);
+        tiles += sbk::lane_tiles(lane_width(d, i), t.shift[i]);
     }
     t.off[d->k] = d->lane_off[d->k];
     t.tile0[d->k] = tiles;

@@ -18,10 +18,13 @@ LOGIT_REL = 2e-3
 LSE_REL = 1e-4
 
 
-def upload(d, device="cuda", lanes_separate=False, pad_w=0, pad_x=0, pad_bits=0x7FC0):
+def upload(d, device="cuda", lanes_separate=False, pad_w=0, pad_x=0, pad_bits=0x7FC0,
+           lane_base_bytes=None):
     """Device tensors for a workload dict; optionally each lane in its own
     allocation and/or row padding filled with ``pad_bits`` (NaN by default)
-    that the kernels must never use."""
+    that the kernels must never use.  ``lane_base_bytes`` (with separate
+    lanes) starts lane i's shard that many bytes (a multiple of 16) into its
+    allocation, which the caching allocator aligns to at least 512 bytes."""
     x_bits, w_bits, off = d["x"], d["w"], d["lane_off"]
     B, H = x_bits.shape
     if pad_x:
@@ -37,7 +40,16 @@ def upload(d, device="cuda", lanes_separate=False, pad_w=0, pad_x=0, pad_bits=0x
         for i, wi in enumerate(widths):
             s = np.full((H, ldw), pad_bits, dtype=np.uint16)
             s[:, :wi] = w_bits[:, off[i]:off[i + 1]]
-            shards.append(sb.to_device_bf16(s, device)[:, :wi])
+            if lane_base_bytes is None:
+                shards.append(sb.to_device_bf16(s, device)[:, :wi])
+                continue
+            e = lane_base_bytes[i] // 2
+            assert lane_base_bytes[i] % 16 == 0
+            flat = np.full(H * ldw + e + 64, pad_bits, dtype=np.uint16)
+            flat[e:e + H * ldw] = s.ravel()
+            t = sb.to_device_bf16(flat, device)[e:e + H * ldw].view(H, ldw)
+            assert t.data_ptr() % 128 == lane_base_bytes[i] % 128
+            shards.append(t[:, :wi])
         w = shards
     else:
         w = sb.to_device_bf16(w_bits, device)

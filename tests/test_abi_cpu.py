@@ -72,7 +72,9 @@ def tokens_status(head, ids=FAKE, ws=FAKE, ws_bytes=1 << 30):
 
 def test_workspace_bytes_for_the_workloads():
     h = fake_head(B=16, H=5120, V=151936, off=(0, 37984, 75968, 113952, 151936))
-    T = 4 * 297
+    # tile capacity per lane: ceil((37984 + 56) / 128), room for a lane grid
+    # shifted by up to 56 columns onto a cache-line boundary
+    T = 4 * 298
     # completion counters (256 B), per-tile pairs, per-lane pairs
     assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == 256 + 16 * T * 8 + 512
     lp = sb.sb_workspace_bytes(h, sb.SB_SURF_LOGPROBS)

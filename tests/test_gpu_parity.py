@@ -76,6 +76,25 @@ def test_non_finite_padding_is_never_read(require_gpu, B):
     assert np.array_equal(g["logits"], g2["logits"])
 
 
+@pytest.mark.parametrize("B", [16, 40, 300])
+def test_lane_base_alignment(require_gpu, B):
+    """Shards that start at 16-byte positions inside a 128-byte cache line
+    (each lane's tile grid then starts up to 56 columns before its first
+    column; a lane of 8 or 100 columns gains a tile): IDs and logits
+    bit-identical to line-aligned shards (each logit's sum order depends on H
+    only), lse within a few ulp (its per-tile partial sums group the columns
+    differently), and everything equal to the oracle."""
+    H, V = 136, 3000
+    off = [0, 712, 720, 820, 3000]
+    d = inputs.make_random(B, H, V, off, seed=11 + B)
+    ref = run_surfaces(upload(d, lanes_separate=True, lane_base_bytes=[0, 0, 0, 0]))
+    for bases in ([16, 48, 64, 112], [96, 112, 112, 0], [112, 16, 80, 48]):
+        g, _, _ = _case(d, lanes_separate=True, lane_base_bytes=bases)
+        for key in ("ids_tok", "ids_lp", "ids_r0", "logits"):
+            assert np.array_equal(g[key], ref[key]), (bases, key)
+        np.testing.assert_allclose(g["lse"], ref["lse"], rtol=4e-7, atol=0)
+
+
 def test_empty_hidden_size(require_gpu):
     B, V = 3, 1000
     x = torch.empty((B, 0), dtype=torch.bfloat16, device="cuda")
