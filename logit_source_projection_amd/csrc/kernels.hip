@@ -24,7 +24,12 @@
 //     is therefore accumulated in an order fixed by H alone, independent of
 //     the lane split, the column position and the epilogue;
 //   * buffer loads with per-step rebased resources: rows beyond H and
-//     columns beyond the lane's end read as zero without faulting.
+//     columns beyond the lane's end read as zero without faulting;
+//   * weight loads are non-temporal when one row group covers the batch
+//     (every weight byte is then read exactly once), and use the default
+//     policy when further row groups re-read the tile through the L2;
+//   * a lane's tiles start on 128-byte lines, so that no line is shared by
+//     two tiles.
 #include "kernels.h"
 
 #include <float.h>
@@ -50,6 +55,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
 {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// Cache policy of the weight loads: kPolicyStream marks them non-temporal
+// (each weight byte is read by one workgroup only and should not displace
+// the hidden rows, which every workgroup re-reads); kPolicyShared keeps the
+// default policy, for tiles that several row groups read through the L2.
+constexpr int kPolicyShared = 0;
+constexpr int kPolicyStream = 2;  // the nt bit of the buffer instruction
+
+template <int POL>
+__device__ __forceinline__ u32x4 load16w(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, POL));
 }
 
 // (value, index) order: larger value first, then lower index.
@@ -103,7 +121,7 @@ struct Frags {
     u32x4 x[MB];
 };
 
-template <int MB>
+template <int MB, int POL>
 __device__ __forceinline__ void load_step(Frags<MB> &f, const uint16_t *wbase, int64_t wbytes,
                                           const uint16_t *xbase, int64_t xbytes, int k0,
                                           int64_t ldw, const uint32_t (&wvo)[8],
@@ -115,7 +133,7 @@ __device__ __forceinline__ void load_step(Frags<MB> &f, const uint16_t *wbase, i
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + k0, xbytes - (int64_t)k0 * 2);
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-        f.w[r] = load16(rw, wvo[r]);
+        f.w[r] = load16w<POL>(rw, wvo[r]);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
         f.x[mb] = load16(rx, xvo[mb]);
@@ -279,7 +297,7 @@ struct Occupancy {
     static constexpr int kBlocksPerCU = MB == 2 ? 2 : 1;
 };
 
-template <int MB, int EPI>
+template <int MB, int EPI, int POL>
 __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_gemm_kernel(const HeadArgs a)
 {
     __shared__ float red[kWaves][kRowBlock][kTileN + 4];
@@ -339,18 +357,18 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
     Frags<MB> fa, fb;
     int s = wave;
     if (s < nsteps)
-        load_step<MB>(fa, wbase, wbytes, xbase, xbytes, s * kStepK, a.ldw, wvo, xvo);
+        load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, s * kStepK, a.ldw, wvo, xvo);
     while (s < nsteps) {
         const int s1 = s + kWaves;
         if (s1 < nsteps)
-            load_step<MB>(fb, wbase, wbytes, xbase, xbytes, s1 * kStepK, a.ldw, wvo, xvo);
+            load_step<MB, POL>(fb, wbase, wbytes, xbase, xbytes, s1 * kStepK, a.ldw, wvo, xvo);
         compute_step<MB>(fa, acc, s * kStepK, H, g);
         s = s1;
         if (s >= nsteps)
             break;
         const int s2 = s + kWaves;
         if (s2 < nsteps)
-            load_step<MB>(fa, wbase, wbytes, xbase, xbytes, s2 * kStepK, a.ldw, wvo, xvo);
+            load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, s2 * kStepK, a.ldw, wvo, xvo);
         compute_step<MB>(fb, acc, s * kStepK, H, g);
         s = s2;
     }
@@ -957,7 +975,7 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int MB>
+template <int MB, int POL>
 hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
 {
     const int rpg = kRowBlock * MB;
@@ -965,16 +983,16 @@ hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
     dim3 grid(((ntiles + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg));
     switch (epi) {
     case kEpiPair:
-        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPair>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPair, POL>), grid, dim3(kThreads), 0, s, a);
         break;
     case kEpiPairLse:
-        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPairLse>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPairLse, POL>), grid, dim3(kThreads), 0, s, a);
         break;
     case kEpiPairLseOut:
-        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPairLseOut>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPairLseOut, POL>), grid, dim3(kThreads), 0, s, a);
         break;
     case kEpiShard:
-        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiShard>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiShard, POL>), grid, dim3(kThreads), 0, s, a);
         break;
     default:
         return hipErrorInvalidValue;
@@ -988,9 +1006,12 @@ hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s)
 {
     if (a.B <= 0 || a.T <= 0)
         return hipSuccess;
+    // one row group: every weight tile is read once, so stream it
     if (rows_per_group(a.B) == kRowBlock)
-        return launch_mb<1>(a, epi, s);
-    return launch_mb<kMaxMB>(a, epi, s);
+        return launch_mb<1, kPolicyStream>(a, epi, s);
+    if (a.B <= kRowBlock * kMaxMB)
+        return launch_mb<kMaxMB, kPolicyStream>(a, epi, s);
+    return launch_mb<kMaxMB, kPolicyShared>(a, epi, s);
 }
 
 hipError_t launch_head_gemm_large(const HeadArgs &a, int epi, hipStream_t s)
