@@ -32,8 +32,10 @@ def parse():
     ap.add_argument("--workload", default="dense_decode",
                     choices=["tiny", "dense_decode", "moe_decode", "large_vocab", "prefill"])
     ap.add_argument("--B", type=int, default=None, help="row count override (large_vocab sweep)")
-    ap.add_argument("--surface", default="tokens",
-                    choices=["tokens", "logprobs", "logprobs_full", "full_logits"])
+    ap.add_argument("--surface", default=None,
+                    choices=["tokens", "logprobs", "logprobs_full", "full_logits"],
+                    help="default: logprobs_full for prefill (complete log-probs + IDs), "
+                         "tokens otherwise")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-report", action="store_true",
                     help="skip the extra surfaces timed for the report")
@@ -222,6 +224,19 @@ class Runner:
         else:
             raise ValueError(surface)
 
+    def time_each(self, surface, steps):
+        """Per-call ms of `steps` calls, each bracketed by its own events."""
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(self.stream)
+            self.call(surface)
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
     def time_calls(self, surface, steps):
         """Average ms per call over `steps` back-to-back calls, with HIP
         events recorded on the stream the kernels run on."""
@@ -237,17 +252,41 @@ class Runner:
         return start.elapsed_time(stop) / steps
 
 
+CPU_SECONDS = 10.0
+
+
 def cpu_baseline(d):
-    """The oracle as it stands, timed on this host's cores, on the whole
-    benchmark input (every row over the whole vocabulary)."""
+    """The oracle as it stands, timed on this host's cores on about
+    CPU_SECONDS of work: whole passes over the benchmark input (every row
+    over the whole vocabulary) when one pass is shorter, else the first rows
+    of the input.  Returns the rate and the oracle's result on those rows."""
+    import numpy as np
     import oracle
+    B = d["B"]
+    probe = min(B, 16)
     t0 = time.perf_counter()
-    z = oracle.logits(d["x"], d["w"])
+    z = oracle.logits(d["x"][:probe], d["w"])
     r = oracle.project(z, d["lane_off"])
-    dt = time.perf_counter() - t0
-    return dict(value=d["B"] / dt, unit="rows/s", cores=oracle.max_threads(), kind="oracle",
-                sample=f"all {d['B']} rows x {d['V']} columns of the benchmark input, one pass "
-                       f"(fp64 logits + per-lane projection + logsumexp), {dt:.2f} s"), r
+    per_row = (time.perf_counter() - t0) / probe
+    if per_row * B <= CPU_SECONDS:
+        rows, passes, dt, t0 = B, 0, 0.0, time.perf_counter()
+        while passes == 0 or dt < CPU_SECONDS:
+            z = oracle.logits(d["x"], d["w"])
+            r = oracle.project(z, d["lane_off"])
+            passes += 1
+            dt = time.perf_counter() - t0
+        what = f"all {B} rows x {d['V']} columns of the benchmark input, {passes} passes"
+    else:
+        rows = max(probe, min(B, int(np.ceil(CPU_SECONDS / per_row))))
+        t0 = time.perf_counter()
+        z = oracle.logits(d["x"][:rows], d["w"])
+        r = oracle.project(z, d["lane_off"])
+        passes, dt = 1, time.perf_counter() - t0
+        what = f"first {rows} of {B} rows x {d['V']} columns of the benchmark input, one pass"
+    return dict(value=rows * passes / dt, unit="rows/s", cores=oracle.max_threads(),
+                kind="oracle",
+                sample=f"{what} (fp64 logits + per-lane projection + logsumexp), "
+                       f"{dt:.2f} s"), r, rows
 
 
 def main():
@@ -265,6 +304,8 @@ def main():
     import torch
     from logit_source_projection_amd import inputs
 
+    if args.surface is None:
+        args.surface = "logprobs_full" if args.workload == "prefill" else "tokens"
     t0 = time.perf_counter()
     d = inputs.make_workload(args.workload, B=args.B)
     gen_s = time.perf_counter() - t0
@@ -326,6 +367,12 @@ def main():
             ids_identical=same,
             bytes_out_tokens=4 * B, bytes_out_full_logits=4 * B * d["V"],
             result_cut_percent=result_cut_percent(4 * B, 4 * B * d["V"]))
+        each = run.time_each(args.surface, args.steps)
+        report["per_call_ms"] = dict(
+            surface=args.surface, calls=len(each),
+            median=round(float(np.median(each)), 4),
+            p10=round(float(np.percentile(each, 10)), 4),
+            p90=round(float(np.percentile(each, 90)), 4))
         ms_lp = run.time_calls("logprobs", 10)
         report["logprobs_ms"] = round(ms_lp, 4)
         report["tokens_per_s"] = rows_s
@@ -336,11 +383,12 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu, r = cpu_baseline(d)
+        cpu, r, nrows = cpu_baseline(d)
         if not args.no_report:
             ok = ~r["near_tie"]
             got = run.ids.cpu().numpy() if args.surface != "full_logits" else run.ids_r0.cpu().numpy()
-            report["ids_match_oracle"] = bool(np.array_equal(got[ok], r["ids"][ok]))
+            report["ids_match_oracle"] = bool(np.array_equal(got[:nrows][ok], r["ids"][ok]))
+            report["ids_checked_rows"] = nrows
             report["near_tie_rows"] = [int(i) for i in np.nonzero(r["near_tie"])[0]]
 
     line = {
