@@ -78,7 +78,7 @@ typedef enum sb_status {
                                 a logits / log-probs leading dim not a
                                 multiple of 4                                  */
     SB_ERR_WORKSPACE = -5,   /* workspace smaller than sb_workspace_bytes()   */
-    SB_ERR_UNSUPPORTED = -6, /* B > 65535, or 40 shard rows or 32 rows of x
+    SB_ERR_UNSUPPORTED = -6, /* B > 65535, or 40 shard rows or 64 rows of x
                                 span 4 GiB or more                            */
     SB_ERR_HIP = -7          /* a HIP launch failed                            */
 } sb_status;

@@ -11,7 +11,7 @@ constexpr int kTileN = 128;     // vocab columns per workgroup tile
 constexpr int kStepK = 32;      // hidden rows per MFMA step (16x16x32 bf16)
 constexpr int kWaves = 4;       // waves per workgroup; K steps interleaved over them
 constexpr int kRowBlock = 16;   // rows per MFMA row block
-constexpr int kMaxMB = 2;       // row blocks per workgroup
+constexpr int kMaxMB = 4;       // row blocks per workgroup
 constexpr int kArgmaxChunk = 8192;  // columns per workgroup in the full-logit argmax
 constexpr int kLineBytes = 128;     // L2 cache line
 // A lane's tile grid starts up to this many columns before its first column,
@@ -67,10 +67,14 @@ struct HeadArgs {
 // Tiles of a lane of vi columns whose grid starts `shift` columns early.
 inline int lane_tiles(int vi, int shift) { return (vi + shift + kTileN - 1) / kTileN; }
 
-// Rows per workgroup row group for a batch of B rows: one 16-row MFMA block
-// up to 16 rows, two above (more rows run as further row groups, dispatched
-// right after each other on the same weight tile).
-inline int rows_per_group(int B) { return B <= kRowBlock ? kRowBlock : 2 * kRowBlock; }
+// Rows per workgroup row group for a batch of B rows: one, two or four
+// 16-row MFMA blocks, so that up to 64 rows read each weight tile once (more
+// rows run as further row groups, dispatched right after each other on the
+// same weight tile).
+inline int rows_per_group(int B)
+{
+    return B <= kRowBlock ? kRowBlock : (B <= 2 * kRowBlock ? 2 * kRowBlock : kMaxMB * kRowBlock);
+}
 
 // Launch the head GEMM with the given epilogue.  For every epilogue except
 // kEpiShard the launch also produces ids (and lse / sel_lp when non-null)

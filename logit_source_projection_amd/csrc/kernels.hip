@@ -10,7 +10,8 @@
 // Mainloop design (decode shapes are HBM-bound: every weight byte is used by
 // B <= 64 rows only):
 //   * one workgroup = 4 waves = one 128-column tile of one lane, rows
-//     [m0, m0 + 16*MB);
+//     [m0, m0 + 16*MB) with MB = 1, 2 or 4, so that up to 64 rows read each
+//     weight tile once;
 //   * W is row-major along the vocabulary (column-contiguous), while the
 //     16x16x32 bf16 MFMA wants 8 consecutive K values per lane.  Each lane
 //     loads 8 rows x 8 columns (eight 16-byte loads, 256-byte contiguous
@@ -289,12 +290,12 @@ __device__ void finish_tile(const HeadArgs &a, int lane, int group, int m0, int 
 }
 
 // Minimum workgroups per CU handed to the register allocator.  One row block
-// is left unconstrained (it settles at 3 waves per SIMD; squeezing it into
-// 128 registers for a 4th wave costs a third of the bandwidth); two row
-// blocks are held to 2 waves per SIMD.
+// is left unconstrained (it fits 128 registers: 4 waves per SIMD); two row
+// blocks are held to 3 waves per SIMD (168 registers) and four to 2 (256),
+// both without spills.
 template <int MB>
 struct Occupancy {
-    static constexpr int kBlocksPerCU = MB == 2 ? 2 : 1;
+    static constexpr int kBlocksPerCU = MB == 1 ? 1 : (MB == 2 ? 3 : 2);
 };
 
 template <int MB, int EPI, int POL>
@@ -353,25 +354,27 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
         for (int c = 0; c < 8; ++c)
             acc[mb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // This wave's steps are wave, wave + 4, ...: nw of them, taken in pairs
+    // (one step loading while the other computes) with a single exit at the
+    // end of a pair, so that the accumulators stay in place.
     const int nsteps = (H + kStepK - 1) / kStepK;
+    const int nw = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;
     Frags<MB> fa, fb;
-    int s = wave;
-    if (s < nsteps)
-        load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, s * kStepK, a.ldw, wvo, xvo);
-    while (s < nsteps) {
-        const int s1 = s + kWaves;
-        if (s1 < nsteps)
-            load_step<MB, POL>(fb, wbase, wbytes, xbase, xbytes, s1 * kStepK, a.ldw, wvo, xvo);
-        compute_step<MB>(fa, acc, s * kStepK, H, g);
-        s = s1;
-        if (s >= nsteps)
-            break;
-        const int s2 = s + kWaves;
-        if (s2 < nsteps)
-            load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, s2 * kStepK, a.ldw, wvo, xvo);
-        compute_step<MB>(fb, acc, s * kStepK, H, g);
-        s = s2;
+    if (nw > 0)
+        load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, wave * kStepK, a.ldw, wvo, xvo);
+    int k0 = wave * kStepK;
+    for (int i = 0; i + 2 <= nw; i += 2) {
+        load_step<MB, POL>(fb, wbase, wbytes, xbase, xbytes, k0 + kWaves * kStepK, a.ldw, wvo,
+                           xvo);
+        compute_step<MB>(fa, acc, k0, H, g);
+        if (i + 2 < nw)
+            load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, k0 + 2 * kWaves * kStepK, a.ldw,
+                               wvo, xvo);
+        compute_step<MB>(fb, acc, k0 + kWaves * kStepK, H, g);
+        k0 += 2 * kWaves * kStepK;
     }
+    if (nw & 1)
+        compute_step<MB>(fa, acc, k0, H, g);
 
     // ---------------- epilogue, one 16-row block at a time ----------------
     const int erow = threadIdx.x >> 4;  // 0..15: row inside the block
@@ -1007,11 +1010,16 @@ hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s)
     if (a.B <= 0 || a.T <= 0)
         return hipSuccess;
     // one row group: every weight tile is read once, so stream it
-    if (rows_per_group(a.B) == kRowBlock)
+    switch (rows_per_group(a.B) / kRowBlock) {
+    case 1:
         return launch_mb<1, kPolicyStream>(a, epi, s);
-    if (a.B <= kRowBlock * kMaxMB)
-        return launch_mb<kMaxMB, kPolicyStream>(a, epi, s);
-    return launch_mb<kMaxMB, kPolicyShared>(a, epi, s);
+    case 2:
+        return launch_mb<2, kPolicyStream>(a, epi, s);
+    default:
+        if (a.B <= kRowBlock * kMaxMB)
+            return launch_mb<kMaxMB, kPolicyStream>(a, epi, s);
+        return launch_mb<kMaxMB, kPolicyShared>(a, epi, s);
+    }
 }
 
 hipError_t launch_head_gemm_large(const HeadArgs &a, int epi, hipStream_t s)

@@ -49,6 +49,8 @@ SMALL = [
     (33, 1000, 777, [0, 300, 777], True),
     (64, 4096, 2048, [0, 1024, 2048], False),
     (65, 128, 1000, [0, 13, 500, 1000], True),
+    (48, 136, 2000, [0, 1000, 2000], False),
+    (100, 40, 1000, [0, 504, 1000], True),
     (130, 72, 1536, [0, 512, 1024, 1536], False),
     (5, 8, 100, [0, 50, 100], True),
     (3, 40, 129, [0, 129], True),
