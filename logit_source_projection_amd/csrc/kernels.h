@@ -49,16 +49,17 @@ struct HeadArgs {
     int64_t ldw;
     int32_t B, H, V;
     int32_t T;           // row stride of the pair workspaces (>= lanes.tile0[k])
-    int2 *pair;          // [B][T] {float bits of max, global index}
+    int2 *pair;          // [B][T] {float bits of max, global index} (large-batch kernel)
     float2 *mse;         // [B][T] {tile max, sum exp(y - tile max)}
     float *out;          // [B][ldo] fp32 logits at global columns (kEpiPairLseOut)
     int64_t ldo;
-    // Completion protocol of the token / log-prob surfaces: the workgroup
-    // that finishes a lane's last tile folds that lane, the one that finishes
-    // a row group's last lane folds the lanes into ids / lse / sel_lp.
-    uint32_t *sync;      // [row groups][k + 1] counters: zero on entry, left zero
-    int2 *lane_pair;     // [B][k] per-lane {max bits, global index}
-    float2 *lane_mse;    // [B][k] per-lane {max, sum exp(y - max)}
+    // Completion protocol of the token / log-prob surfaces (head_gemm_kernel):
+    // per-lane keys merged by atomic maximum; the workgroup that finishes a
+    // row group's last tile (tokens) or last lane (log-probs) writes ids /
+    // lse / sel_lp.
+    uint32_t *sync;              // [row groups][k + 1] counters: zero on entry, left zero
+    unsigned long long *keys;    // [B][k] per-lane (max, lowest index) keys: zero on entry, left zero
+    float2 *lane_mse;            // [B][k] per-lane {max, sum exp(y - max)}
     int32_t *ids;        // [B]
     float *lse;          // [B] or null
     float *sel_lp;       // [B] or null

@@ -181,12 +181,104 @@ __device__ __forceinline__ void compute_step(Frags<MB> &f, f32x4 (&acc)[MB][8], 
     }
 }
 
-// Completion protocol, run by every workgroup after its tile's (row, tile)
-// results are stored.  The workgroup that completes the last tile of a lane
-// (for its row group) folds that lane's tiles in a fixed order into one
-// result per row -- the paper's one int32 result per lane -- and the one that
-// completes the last lane folds the k lane results in ascending lane order.
-// Counters are left at zero for the next call on the same workspace.
+// (value, global index) as one 64-bit key whose unsigned order is value
+// ascending, then index descending: the largest key is the largest value at
+// its lowest index, and merging keys with an atomic maximum gives the same
+// result in any order.  -0 is taken as +0, so equal values always tie.
+__device__ __forceinline__ unsigned long long pack_key(float v, int idx)
+{
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u)
+        u = 0u;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ float key_value(unsigned long long key)
+{
+    const uint32_t u = (uint32_t)(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+__device__ __forceinline__ int key_index(unsigned long long key)
+{
+    return (int)(0xFFFFFFFFu - (uint32_t)key);
+}
+
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o, int w)
+{
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, w);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, w);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Threads per row when the workgroup's 256 threads fold `rows` rows: a power
+// of two, at most one wave, so that a row's threads sit in one wave.
+__device__ __forceinline__ int fold_width(int rows)
+{
+    int w = 64;
+    while (w > 1 && w * rows > kThreads)
+        w >>= 1;
+    return w;
+}
+
+// The k lane keys of a row folded into its token ID (and, for the log-prob
+// surfaces, the lane (max, sum-exp) pairs into lse), then the keys cleared.
+// Thread j of a row takes lanes j, j + w, ... in ascending order; the w
+// partial results are combined by a fixed butterfly.
+template <int EPI>
+__device__ void finish_group(const HeadArgs &a, int m0, int rows_here)
+{
+    const int k = a.lanes.k;
+    const int w = fold_width(rows_here);
+    const int r = threadIdx.x / w, j = threadIdx.x % w;
+    const bool rowok = r < rows_here;
+    const int row = m0 + r;
+    unsigned long long best = 0;
+    float m = -INFINITY, se = 0.f;
+    if (rowok) {
+        for (int i = j; i < k; i += w) {
+            unsigned long long *kp = a.keys + (int64_t)row * k + i;
+            const unsigned long long key = __hip_atomic_load(kp, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(kp, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            best = key > best ? key : best;
+            if (EPI != kEpiPair) {
+                const float2 q = a.lane_mse[(int64_t)row * k + i];
+                lse_merge(m, se, q.x, q.y);
+            }
+        }
+    }
+    for (int o = w / 2; o >= 1; o >>= 1) {
+        const unsigned long long ok = shfl_xor_u64(best, o, w);
+        best = ok > best ? ok : best;
+        if (EPI != kEpiPair) {
+            const float om = __shfl_xor(m, o, w);
+            const float os = __shfl_xor(se, o, w);
+            lse_merge(m, se, om, os);
+        }
+    }
+    if (rowok && j == 0) {
+        a.ids[row] = key_index(best);
+        if (EPI != kEpiPair) {
+            const float l = m + __logf(se);
+            if (a.lse)
+                a.lse[row] = l;
+            if (a.sel_lp)
+                a.sel_lp[row] = key_value(best) - l;
+        }
+    }
+}
+
+// Completion protocol, run by every workgroup after its tile's results are
+// published.  Token IDs: every (row, tile) maximum has been merged into the
+// row's key of its lane with an atomic maximum -- the paper's one int32
+// result per lane -- so the workgroup that completes the row group's last
+// tile only folds the k lane keys of each row.  Log-prob surfaces: the
+// (tile max, sum-exp) pairs are written through; the workgroup that
+// completes a lane's last tile folds them in a fixed order into the lane's
+// pair, and the one that completes the last lane folds the lanes.  Counters
+// and keys are left at zero for the next call on the same workspace.
 template <int MB, int EPI>
 __device__ void finish_tile(const HeadArgs &a, int lane, int group, int m0, int rows_here)
 {
@@ -194,10 +286,25 @@ __device__ void finish_tile(const HeadArgs &a, int lane, int group, int m0, int 
     const int k = a.lanes.k;
     uint32_t *lane_ctr = a.sync + (int64_t)group * (k + 1) + lane;
     uint32_t *group_ctr = a.sync + (int64_t)group * (k + 1) + k;
-    const int t0 = a.lanes.tile0[lane], t1 = a.lanes.tile0[lane + 1];
 
-    wait_all_memory();  // this wave's written-through results are in memory
+    wait_all_memory();  // this wave's atomics and written-through results are done
     __syncthreads();    // ... and every other wave's
+    if (EPI == kEpiPair) {
+        if (threadIdx.x == 0) {
+            const uint32_t old = atomicAdd(group_ctr, 1u);
+            s_last = old == (uint32_t)(a.lanes.tile0[k] - 1);
+        }
+        __syncthreads();
+        if (!s_last)
+            return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        finish_group<EPI>(a, m0, rows_here);
+        if (threadIdx.x == 0)
+            __hip_atomic_store(group_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+
+    const int t0 = a.lanes.tile0[lane], t1 = a.lanes.tile0[lane + 1];
     if (threadIdx.x == 0) {
         const uint32_t old = atomicAdd(lane_ctr, 1u);
         s_last = old == (uint32_t)(t1 - t0 - 1);
@@ -208,44 +315,31 @@ __device__ void finish_tile(const HeadArgs &a, int lane, int group, int m0, int 
     // acquire: drop stale cached copies before reading the lane's results
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-    constexpr int TPR = kThreads / (kRowBlock * MB);  // threads per row
-    const int r = threadIdx.x / TPR, j = threadIdx.x % TPR;
-    const int b = m0 + r;
-    const bool rowok = r < rows_here;
-    float bv = -INFINITY, m = -INFINITY, se = 0.f;
-    int bi = INT_MAX;
-    if (rowok) {
-        for (int t = t0 + j; t < t1; t += TPR) {
-            const int64_t idx = (int64_t)b * a.T + t;
-            const int2 p = a.pair[idx];
-            const float pv = __int_as_float(p.x);
-            if (better(pv, p.y, bv, bi)) {
-                bv = pv;
-                bi = p.y;
-            }
-            if (EPI != kEpiPair) {
-                const float2 q = a.mse[idx];
-                lse_merge(m, se, q.x, q.y);
-            }
-        }
-    }
+    // Thread j of a row merges tiles t0 + j, t0 + j + w, ... in ascending
+    // order (loads issued four at a time), then a fixed butterfly.
+    {
+        const int w = fold_width(rows_here);
+        const int r = threadIdx.x / w, j = threadIdx.x % w;
+        const int b = m0 + r;
+        float m = -INFINITY, se = 0.f;
+        if (r < rows_here) {
+            const float2 *row = a.mse + (int64_t)b * a.T;
+            for (int t = t0 + j; t < t1; t += 4 * w) {
+                float2 q[4];
 #pragma unroll
-    for (int o = TPR / 2; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, TPR);
-        const int oi = __shfl_xor(bi, o, TPR);
-        if (better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
+                for (int u = 0; u < 4; ++u)
+                    q[u] = t + u * w < t1 ? row[t + u * w] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    lse_merge(m, se, q[u].x, q[u].y);
+            }
         }
-        if (EPI != kEpiPair) {
-            const float om = __shfl_xor(m, o, TPR);
-            const float os = __shfl_xor(se, o, TPR);
+        for (int o = w / 2; o >= 1; o >>= 1) {
+            const float om = __shfl_xor(m, o, w);
+            const float os = __shfl_xor(se, o, w);
             lse_merge(m, se, om, os);
         }
-    }
-    if (rowok && j == 0) {
-        store_through(&a.lane_pair[(int64_t)b * k + lane], __float_as_uint(bv), (uint32_t)bi);
-        if (EPI != kEpiPair)
+        if (r < rows_here && j == 0)
             store_through(&a.lane_mse[(int64_t)b * k + lane], __float_as_uint(m),
                           __float_as_uint(se));
     }
@@ -260,31 +354,7 @@ __device__ void finish_tile(const HeadArgs &a, int lane, int group, int m0, int 
     if (!s_last)
         return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (threadIdx.x < rows_here) {
-        const int row = m0 + threadIdx.x;
-        float rv = -INFINITY, rm = -INFINITY, rs = 0.f;
-        int ri = INT_MAX;
-        for (int i = 0; i < k; ++i) {
-            const int2 p = a.lane_pair[(int64_t)row * k + i];
-            const float pv = __int_as_float(p.x);
-            if (better(pv, p.y, rv, ri)) {
-                rv = pv;
-                ri = p.y;
-            }
-            if (EPI != kEpiPair) {
-                const float2 q = a.lane_mse[(int64_t)row * k + i];
-                lse_merge(rm, rs, q.x, q.y);
-            }
-        }
-        a.ids[row] = ri;
-        if (EPI != kEpiPair) {
-            const float l = rm + __logf(rs);
-            if (a.lse)
-                a.lse[row] = l;
-            if (a.sel_lp)
-                a.sel_lp[row] = rv - l;
-        }
-    }
+    finish_group<EPI>(a, m0, rows_here);
     if (threadIdx.x == 0)
         __hip_atomic_store(group_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -467,10 +537,11 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
                     se += __shfl_xor(se, o, 16);
             }
             if (cg == 0 && rowok) {
-                const int64_t idx = (int64_t)b * a.T + tile;
-                store_through(&a.pair[idx], __float_as_uint(bv), (uint32_t)bi);
+                __hip_atomic_fetch_max(a.keys + (int64_t)b * a.lanes.k + lane, pack_key(bv, bi),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (EPI != kEpiPair)
-                    store_through(&a.mse[idx], __float_as_uint(bv), __float_as_uint(se));
+                    store_through(&a.mse[(int64_t)b * a.T + tile], __float_as_uint(bv),
+                                  __float_as_uint(se));
             }
         }
     }

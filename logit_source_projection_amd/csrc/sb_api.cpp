@@ -73,7 +73,7 @@ struct Layout {
     int T = 0;            // tile capacity: row stride of the (row, tile) regions
     int nchunks = 0;      // full-logit argmax chunks per row
     int groups = 0;       // row groups (grid y) of the head GEMM
-    size_t sync = 0, pair = 0, mse = 0, lane_pair = 0, lane_mse = 0;
+    size_t sync = 0, keys = 0, pair = 0, mse = 0, lane_mse = 0;
     size_t shard[SB_MAX_LANES] = {}, partial = 0;
     size_t total = 0;
 };
@@ -92,28 +92,34 @@ Layout layout(const sb_head_desc *d, int surface)
         return L;
     const int rpg = sbk::rows_per_group(d->B);
     L.groups = (d->B + rpg - 1) / rpg;
+    const bool large = d->B >= sbk::kLargeBatch;
+    const bool lse = surface == SB_SURF_LOGPROBS || surface == SB_SURF_LOGPROBS_FULL;
     switch (surface) {
     case SB_SURF_TOKENS:
-        // completion counters first: the region that must start zeroed
-        L.sync = at;
-        at = align_up(at + (size_t)L.groups * (d->k + 1) * sizeof(uint32_t), kRegionAlign);
-        L.pair = at;
-        at = align_up(at + B * L.T * sizeof(int2), kRegionAlign);
-        L.lane_pair = at;
-        at = align_up(at + B * d->k * sizeof(int2), kRegionAlign);
-        break;
     case SB_SURF_LOGPROBS:
     case SB_SURF_LOGPROBS_FULL:
+        if (large) {
+            // large-batch kernel: (row, tile) results, folded by the combine kernel
+            L.pair = at;
+            at = align_up(at + B * L.T * sizeof(int2), kRegionAlign);
+            if (lse) {
+                L.mse = at;
+                at = align_up(at + B * L.T * sizeof(float2), kRegionAlign);
+            }
+            break;
+        }
+        // completion counters and lane keys first: the regions that must
+        // start zeroed (every call leaves them zeroed)
         L.sync = at;
         at = align_up(at + (size_t)L.groups * (d->k + 1) * sizeof(uint32_t), kRegionAlign);
-        L.pair = at;
-        at = align_up(at + B * L.T * sizeof(int2), kRegionAlign);
-        L.mse = at;
-        at = align_up(at + B * L.T * sizeof(float2), kRegionAlign);
-        L.lane_pair = at;
-        at = align_up(at + B * d->k * sizeof(int2), kRegionAlign);
-        L.lane_mse = at;
-        at = align_up(at + B * d->k * sizeof(float2), kRegionAlign);
+        L.keys = at;
+        at = align_up(at + B * d->k * sizeof(uint64_t), kRegionAlign);
+        if (lse) {
+            L.mse = at;
+            at = align_up(at + B * L.T * sizeof(float2), kRegionAlign);
+            L.lane_mse = at;
+            at = align_up(at + B * d->k * sizeof(float2), kRegionAlign);
+        }
         break;
     case SB_SURF_FULL_LOGITS:
         for (int i = 0; i < d->k; ++i) {
@@ -167,7 +173,7 @@ void fill_args(const sb_head_desc *d, const Layout &L, sbk::HeadArgs &a)
     a.out = nullptr;
     a.ldo = 0;
     a.sync = nullptr;
-    a.lane_pair = nullptr;
+    a.keys = nullptr;
     a.lane_mse = nullptr;
     a.ids = nullptr;
     a.lse = nullptr;
@@ -225,17 +231,17 @@ sb_status sb_project_tokens(const sb_head_desc *desc, int32_t *ids, void *ws, si
     hipStream_t s = static_cast<hipStream_t>(stream);
     sbk::HeadArgs a;
     fill_args(desc, L, a);
-    a.sync = region<uint32_t>(ws, L.sync);
-    a.pair = region<int2>(ws, L.pair);
-    a.lane_pair = region<int2>(ws, L.lane_pair);
     a.ids = ids;
     if (a.B >= sbk::kLargeBatch) {
+        a.pair = region<int2>(ws, L.pair);
         if (sbk::launch_head_gemm_large(a, sbk::kEpiPair, s) != hipSuccess ||
             sbk::launch_combine(a.pair, nullptr, a.lanes, a.B, a.T, ids, nullptr, nullptr, s) !=
                 hipSuccess)
             return SB_ERR_HIP;
         return SB_OK;
     }
+    a.sync = region<uint32_t>(ws, L.sync);
+    a.keys = region<unsigned long long>(ws, L.keys);
     if (sbk::launch_head_gemm(a, sbk::kEpiPair, s) != hipSuccess)
         return SB_ERR_HIP;
     return SB_OK;
@@ -264,11 +270,14 @@ sb_status sb_project_logprobs(const sb_head_desc *desc, int32_t *ids, float *lse
     hipStream_t s = static_cast<hipStream_t>(stream);
     sbk::HeadArgs a;
     fill_args(desc, L, a);
-    a.sync = region<uint32_t>(ws, L.sync);
-    a.pair = region<int2>(ws, L.pair);
     a.mse = region<float2>(ws, L.mse);
-    a.lane_pair = region<int2>(ws, L.lane_pair);
-    a.lane_mse = region<float2>(ws, L.lane_mse);
+    if (a.B >= sbk::kLargeBatch) {
+        a.pair = region<int2>(ws, L.pair);
+    } else {
+        a.sync = region<uint32_t>(ws, L.sync);
+        a.keys = region<unsigned long long>(ws, L.keys);
+        a.lane_mse = region<float2>(ws, L.lane_mse);
+    }
     a.ids = ids;
     a.lse = lse;
     a.sel_lp = sel_lp;

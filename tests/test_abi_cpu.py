@@ -75,10 +75,14 @@ def test_workspace_bytes_for_the_workloads():
     # tile capacity per lane: ceil((37984 + 56) / 128), room for a lane grid
     # shifted by up to 56 columns onto a cache-line boundary
     T = 4 * 298
-    # completion counters (256 B), per-tile pairs, per-lane pairs
-    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == 256 + 16 * T * 8 + 512
+    # completion counters (256 B), per-lane keys (16 rows x 4 lanes x 8 B)
+    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == 256 + 512
+    # + per-tile (max, sum-exp) pairs and per-lane pairs
     lp = sb.sb_workspace_bytes(h, sb.SB_SURF_LOGPROBS)
-    assert lp >= 2 * 16 * T * 8
+    assert lp == 256 + 512 + 16 * T * 8 + 512
+    # large batches: per-tile pairs for the combine kernel only
+    hl = fake_head(B=300, H=5120, V=151936, off=(0, 37984, 75968, 113952, 151936))
+    assert sb.sb_workspace_bytes(hl, sb.SB_SURF_TOKENS) == (300 * T * 8 + 255) // 256 * 256
     full = sb.sb_workspace_bytes(h, sb.SB_SURF_FULL_LOGITS)
     assert full >= 16 * 151936 * 4
     assert sb.sb_workspace_bytes(fake_head(B=0), sb.SB_SURF_TOKENS) == 0
