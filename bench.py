@@ -125,10 +125,12 @@ def record_traffic(args):
     rec = {}
     for which, path in zip(("fetch", "write"), args.record_traffic):
         per = _counter_per_dispatch(path)
-        copy = [v for k, vs in per.items() if "copyBuffer" in k for v in vs]
+        # the calibration copy is the largest copy dispatch (small uploads
+        # of the inputs may be copies too)
+        copy = sorted(v for k, vs in per.items() if "copyBuffer" in k for v in vs)[-1:]
         heads = {k: vs for k, vs in per.items() if "head_gemm" in k}
-        if len(copy) != 1 or not heads:
-            sys.exit(f"{path}: expected one copy dispatch and head kernel dispatches")
+        if not copy or not heads:
+            sys.exit(f"{path}: expected a copy dispatch and head kernel dispatches")
         name, vals = max(heads.items(), key=lambda kv: len(kv[1]))
         factor = calib / (copy[0] * 1024.0)
         kib = sum(vals) / len(vals)
@@ -291,6 +293,8 @@ def cpu_baseline(d):
 
 def main():
     args = parse()
+    if args.surface is None:
+        args.surface = "logprobs_full" if args.workload == "prefill" else "tokens"
     if args.record_traffic:
         record_traffic(args)
         return
@@ -304,8 +308,6 @@ def main():
     import torch
     from logit_source_projection_amd import inputs
 
-    if args.surface is None:
-        args.surface = "logprobs_full" if args.workload == "prefill" else "tokens"
     t0 = time.perf_counter()
     d = inputs.make_workload(args.workload, B=args.B)
     gen_s = time.perf_counter() - t0
