@@ -627,22 +627,41 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const int2 *pair, con
     }
 }
 
+// Each workgroup covers kNormCols columns of one row: every thread loads
+// kNormVec 16-byte vectors (all loads issued before the first store), each
+// load instruction of the workgroup reading 4 KB contiguous.  The row is
+// 16-byte aligned (the ABI requires it); the row's tail is done per element.
+constexpr int kNormVec = 4;
+constexpr int kNormCols = kThreads * 4 * kNormVec;
+
 __global__ __launch_bounds__(kThreads) void normalize_kernel(float *lp, int64_t ld,
                                                              const float *lse, int V)
 {
     const int b = blockIdx.y;
-    const int col = (blockIdx.x * kThreads + threadIdx.x) * 4;
-    if (col >= V)
-        return;
+    const int c0 = blockIdx.x * kNormCols + 4 * threadIdx.x;
     const float l = lse[b];
-    float *p = lp + (int64_t)b * ld + col;
-    if (col + 4 <= V && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
-        f32x4 v = *reinterpret_cast<f32x4 *>(p);
-        v -= l;
-        *reinterpret_cast<f32x4 *>(p) = v;
-    } else {
-        for (int j = 0; j < 4 && col + j < V; ++j)
-            p[j] -= l;
+    float *row = lp + (int64_t)b * ld;
+    if (blockIdx.x * kNormCols + kNormCols <= V) {
+        f32x4 v[kNormVec];
+#pragma unroll
+        for (int j = 0; j < kNormVec; ++j)
+            v[j] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4 *>(row + c0 + 4 * kThreads * j));
+#pragma unroll
+        for (int j = 0; j < kNormVec; ++j)
+            __builtin_nontemporal_store(v[j] - l,
+                                        reinterpret_cast<f32x4 *>(row + c0 + 4 * kThreads * j));
+        return;
+    }
+    for (int j = 0; j < kNormVec; ++j) {
+        const int c = c0 + 4 * kThreads * j;
+        if (c + 4 <= V) {
+            f32x4 *p = reinterpret_cast<f32x4 *>(row + c);
+            *p = *p - l;
+        } else {
+            for (int e = c; e < V; ++e)
+                row[e] -= l;
+        }
     }
 }
 
@@ -966,8 +985,10 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
                                  : a.out + (int64_t)b * a.ldo + gcol;
                 if (rowok) {
                     if (nvalid == 8 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                        *reinterpret_cast<f32x4 *>(dst) = f32x4{y[0], y[1], y[2], y[3]};
-                        *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{y[4], y[5], y[6], y[7]};
+                        __builtin_nontemporal_store(f32x4{y[0], y[1], y[2], y[3]},
+                                                    reinterpret_cast<f32x4 *>(dst));
+                        __builtin_nontemporal_store(f32x4{y[4], y[5], y[6], y[7]},
+                                                    reinterpret_cast<f32x4 *>(dst + 4));
                     } else {
 #pragma unroll
                         for (int c = 0; c < 8; ++c)
@@ -1127,7 +1148,7 @@ hipError_t launch_normalize(float *lp, int64_t ld, const float *lse, int32_t B, 
 {
     if (B <= 0 || V <= 0)
         return hipSuccess;
-    dim3 grid((V + 4 * kThreads - 1) / (4 * kThreads), B);
+    dim3 grid((V + kNormCols - 1) / kNormCols, B);
     hipLaunchKernelGGL(normalize_kernel, grid, dim3(kThreads), 0, s, lp, ld, lse, V);
     return hipGetLastError();
 }
