@@ -105,6 +105,7 @@ def test_workspace_bytes_for_the_workloads():
     (dict(x_ptr=0), sb.SB_ERR_NULL),
     (dict(w_ptrs=[FAKE, 0]), sb.SB_ERR_NULL),
     (dict(B=70000), sb.SB_ERR_UNSUPPORTED),
+    (dict(B=65536), sb.SB_ERR_UNSUPPORTED),
     (dict(ldx=1 << 25), sb.SB_ERR_UNSUPPORTED),  # 64 rows of x span 4 GiB
     (dict(V=(1 << 31) - 8, off=(0, (1 << 31) - 8), ldw=(1 << 31) - 8), sb.SB_ERR_UNSUPPORTED),
 ])

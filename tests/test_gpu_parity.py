@@ -19,11 +19,10 @@ from tests.gpu_common import check_against_oracle, check_internal, run_surfaces,
 pytestmark = pytest.mark.gpu
 
 
-def _case(d, **up):
-    print(f"case {d['name']} B={d['B']} H={d['H']} V={d['V']} lanes={d['lane_off']} {up}",
-          flush=True)
+def _case(d, full_logprobs=True, **up):
+    print(f"case {d['name']} B={d['B']} H={d['H']} V={d['V']} k={d['k']} {up}", flush=True)
     head = upload(d, **up)
-    g = run_surfaces(head)
+    g = run_surfaces(head, full_logprobs=full_logprobs)
     check_internal(g)
     z = oracle.logits(d["x"], d["w"])
     r = check_against_oracle(g, z, d["lane_off"])
@@ -95,6 +94,31 @@ def test_lane_base_alignment(require_gpu, B):
         for key in ("ids_tok", "ids_lp", "ids_r0", "logits"):
             assert np.array_equal(g[key], ref[key]), (bases, key)
         np.testing.assert_allclose(g["lse"], ref["lse"], rtol=4e-7, atol=0)
+
+
+@pytest.mark.parametrize("B", [16, 17, 32, 33, 64, 65, 255, 256, 257])
+def test_batch_boundaries(require_gpu, B):
+    """Both sides of every switch on the batch size: one, two and four row
+    blocks per workgroup, several row groups, the large-batch kernel."""
+    d = inputs.make_random(B, 72, 1000, [0, 504, 1000], seed=1000 + B)
+    _case(d, lanes_separate=(B % 2 == 1))
+
+
+@pytest.mark.parametrize("B,sep", [(16, False), (40, True), (300, False)])
+def test_maximum_lane_count(require_gpu, B, sep):
+    """k = 64 lanes (the ABI's maximum), widths from 8 to 1000 columns."""
+    widths = [(8, 16, 136, 264, 1000, 24, 128, 504)[i % 8] for i in range(64)]
+    off = [0]
+    for wdt in widths:
+        off.append(off[-1] + wdt)
+    d = inputs.make_random(B, 64, off[-1], off, seed=2000 + B)
+    _case(d, lanes_separate=sep)
+
+
+def test_maximum_batch(require_gpu):
+    """B = 65535 (the ABI's maximum): 256 row blocks of the large-batch kernel."""
+    d = inputs.make_random(65535, 40, 520, [0, 256, 520], seed=3000)
+    _case(d, full_logprobs=False)
 
 
 def test_empty_hidden_size(require_gpu):
