@@ -45,9 +45,10 @@
  *    owned by the call until its work completes on the stream; calls that
  *    share one workspace must be ordered on one stream.
  *  - A workspace must be ZERO-FILLED before its first use (allocate it once,
- *    zeroed, and reuse it).  The token and log-prob calls keep completion
- *    counters at its start; every call that completes leaves them zero, so
- *    a workspace stays valid for later calls of any shape.
+ *    zeroed, and reuse it).  For B < 256 the token and log-prob calls keep
+ *    completion counters and per-lane result keys at its start; every call
+ *    that completes leaves them zero, so a workspace stays valid for later
+ *    calls of any shape.
  *
  * Errors
  *  - Validation is synchronous: on any error status nothing is enqueued and
@@ -131,7 +132,8 @@ size_t sb_workspace_bytes(const sb_head_desc *desc, int surface, sb_status *stat
  * ids[b] = lowest global index of max_v z[b][v].  Each lane reduces to one
  * (max, lowest-index) result per row inside the GEMM epilogue; the per-lane
  * results are combined in ascending lane order.  The full logits are never
- * written to memory.  One kernel launch.
+ * written to memory.  One kernel launch for B < 256 (the last workgroup of a
+ * row group writes the IDs); for B >= 256 the GEMM and a combine kernel.
  *   ids  DEVICE int32 [B]
  *   ws   DEVICE workspace of >= sb_workspace_bytes(desc, SB_SURF_TOKENS)
  *        bytes, 16-byte aligned

@@ -21,7 +21,7 @@ Communication Plans):
 * Figure 1 caption: full-logit transfer and source projection deliver the
   same requested token ID.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * the deterministic sampler is greedy argmax over the raw logits, and ties go
   to the lowest global vocabulary index;
