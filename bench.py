@@ -369,6 +369,10 @@ def main():
             ids_identical=same,
             bytes_out_tokens=4 * B, bytes_out_full_logits=4 * B * d["V"],
             result_cut_percent=result_cut_percent(4 * B, 4 * B * d["V"]))
+        from logit_source_projection_amd import selector
+        report["selector"] = selector.report(report["p0_vs_r0"]["ms_tokens"],
+                                             report["p0_vs_r0"]["ms_full_logits"],
+                                             B, d["V"], d["k"])
         each = run.time_each(args.surface, args.steps)
         report["per_call_ms"] = dict(
             surface=args.surface, calls=len(each),
