@@ -171,6 +171,67 @@ sb_status sb_project_logprobs(const sb_head_desc *desc, int32_t *ids,
 sb_status sb_full_logits(const sb_head_desc *desc, float *logits, int64_t ldl,
                          int32_t *ids, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * Partial completion (SemBridge section 6.4, Exact Shards and Partial
+ * Completion; section 3.6, reduction obligations).  The MLP down projection is
+ * row parallel: lane i holds a distinct activation shard X_i [B][K_i] and the
+ * matching weight rows W_i [K_i][N], and produces the incomplete full-width
+ * partial P_i = X_i . W_i (fp32 sums of exact bf16 x bf16 products).  The
+ * registered elementwise operator completes the partials before the output
+ * is exposed:  out = op(...op(op(P_0, P_1), P_2)..., P_{k-1})  (ascending
+ * lane order).  Each P_i is accumulated in an order fixed by the shapes
+ * alone (512-row chunks summed in ascending order), so repeated calls give
+ * bit-identical outputs.
+ * ---------------------------------------------------------------------------
+ */
+typedef enum sb_reduce_op {
+    SB_RED_SUM = 0,
+    SB_RED_PROD = 1,
+    SB_RED_MIN = 2,
+    SB_RED_MAX = 3
+} sb_reduce_op;
+
+/*
+ *   B       rows (tokens); B == 0 is a valid no-op; B <= 65535
+ *   N       output width (the model's hidden size), >= 1
+ *   k       lanes, 1..SB_MAX_LANES
+ *   lane_k  HOST array of k+1 int32 offsets of the reduction dimension:
+ *           0 = lane_k[0] < lane_k[1] < ... < lane_k[k]; K_i = lane_k[i+1] -
+ *           lane_k[i]
+ *   x       HOST array of k DEVICE pointers; x[i] is bf16 [B][ldx], columns
+ *           [0, K_i) used; 16-byte aligned
+ *   ldx     row stride of every x[i], >= max K_i, multiple of 8
+ *   w       HOST array of k DEVICE pointers; w[i] is bf16 [K_i][ldw], columns
+ *           [0, N) used; 16-byte aligned
+ *   ldw     row stride of every w[i], >= N, multiple of 8
+ */
+typedef struct sb_partial_desc {
+    int32_t B, N, k;
+    const int32_t *lane_k;
+    const void *const *x;
+    int64_t ldx;
+    const void *const *w;
+    int64_t ldw;
+} sb_partial_desc;
+
+/*
+ * Bytes of device workspace sb_partial_complete needs on `desc` (the fp32
+ * chunk partials; no zero-fill needed).  Returns 0 and sets *status on an
+ * invalid descriptor (statuses as for the head; SB_ERR_LANES for bad lane_k).
+ */
+size_t sb_partial_workspace_bytes(const sb_partial_desc *desc, sb_status *status);
+
+/*
+ * out[b][n] = op over lanes (ascending) of P_i[b][n].
+ *   op   one of sb_reduce_op (anything else: SB_ERR_SHAPE)
+ *   out  DEVICE fp32 [B][ldo], ldo >= N and a multiple of 4, 16-byte aligned
+ *   ws   >= sb_partial_workspace_bytes(desc) bytes, 16-byte aligned
+ * Two kernel launches: the chunked partial GEMM and the lane reduction.
+ */
+sb_status sb_partial_complete(const sb_partial_desc *desc, int op, float *out, int64_t ldo,
+                              void *ws, size_t ws_bytes, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *sb_status_string(sb_status status);
 

@@ -110,4 +110,33 @@ hipError_t launch_reconstruct(const LaneTable &lanes, int32_t B, float *logits,
 hipError_t launch_row_argmax(const float *logits, int64_t ldl, int32_t B, int32_t V,
                              int2 *partial, int32_t *ids, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Partial completion: lane i holds an activation shard X_i [B][K_i] and the
+// matching weight rows W_i [K_i][N]; its partial is P_i = X_i . W_i, and a
+// registered elementwise operator completes the k partials in lane order.
+// ---------------------------------------------------------------------------
+constexpr int kPartChunk = 512;  // reduction rows per workgroup (split K)
+
+enum ReduceOp : int { kRedSum = 0, kRedProd = 1, kRedMin = 2, kRedMax = 3 };
+
+struct PartialArgs {
+    const uint16_t *x[kMaxLanes];   // lane i's activation shard, bf16 [B][ldx]
+    const uint16_t *w[kMaxLanes];   // lane i's weight rows, bf16 [K_i][ldw]
+    int32_t K[kMaxLanes];           // reduction rows of lane i
+    int32_t chunk0[kMaxLanes + 1];  // first chunk of lane i (prefix sums of ceil(K_i / 512))
+    int64_t ldx, ldw;
+    int32_t B, N, k;
+    int32_t T;                      // 128-column tiles of the output
+    float *part;                    // [chunks][B][ldp] fp32 chunk partials
+    int64_t ldp;
+};
+
+// Chunk partials: part[c][b][n] = sum over the chunk's reduction rows.
+hipError_t launch_partial_gemm(const PartialArgs &a, hipStream_t s);
+
+// out[b][n] = op over lanes (ascending) of the sum over the lane's chunks
+// (ascending).
+hipError_t launch_partial_reduce(const PartialArgs &a, int op, float *out, int64_t ldo,
+                                 hipStream_t s);
+
 }  // namespace sbk

@@ -1095,6 +1095,185 @@ hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Partial completion (row-parallel partials and a registered reduction).
+//
+// The output is only N columns wide (N / 128 tiles), so the reduction
+// dimension is split as well: one workgroup computes a 128-column tile of
+// one 512-row chunk of one lane for 16*MB rows, with the head kernel's
+// mainloop (4 waves, K steps interleaved over the waves, wave-order fold
+// through LDS), and stores the chunk partial in fp32.  The reduce kernel then
+// sums a lane's chunks in ascending order and folds the lanes with the
+// registered operator in ascending order, so every output is computed in an
+// order fixed by the shapes alone.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int find_chunk_lane(const PartialArgs &a, int chunk)
+{
+    int lane = 0;
+    while (lane + 1 < a.k && a.chunk0[lane + 1] <= chunk)
+        ++lane;
+    return lane;
+}
+
+template <int MB, int POL>
+__global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void partial_gemm_kernel(const PartialArgs a)
+{
+    __shared__ float red[kWaves][kRowBlock][kTileN + 4];
+
+    // workgroup id -> (chunk, tile, row group), row groups innermost
+    const int groups = (a.B + kRowBlock * MB - 1) / (kRowBlock * MB);
+    const int group = blockIdx.x % groups;
+    const int rest = blockIdx.x / groups;
+    const int tile = rest % a.T;
+    const int chunk = rest / a.T;
+    if (chunk >= a.chunk0[a.k])
+        return;
+    const int lane = find_chunk_lane(a, chunk);
+    const int r0 = (chunk - a.chunk0[lane]) * kPartChunk;  // first reduction row in the lane
+    const int Hc = min(kPartChunk, a.K[lane] - r0);        // reduction rows of this chunk
+    const int c0 = tile * kTileN;
+    const int m0 = group * (kRowBlock * MB);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int L = threadIdx.x & 63;
+    const int n = L & 15;
+    const int g = L >> 4;
+
+    // readable extents from the chunk's first row and the tile's first
+    // column (reads past them return zeros); hidden positions >= Hc are
+    // masked in registers
+    const uint16_t *wbase = a.w[lane] + (int64_t)r0 * a.ldw + c0;
+    const int64_t wcols = ((int64_t)(a.N - c0) + 7) & ~(int64_t)7;
+    const int64_t wbytes = (((int64_t)(Hc - 1) * a.ldw) + wcols) * 2;
+    const int rows_here = min(a.B - m0, kRowBlock * MB);
+    const uint16_t *xbase = a.x[lane] + (int64_t)m0 * a.ldx + r0;
+    const int64_t xbytes = (((int64_t)(rows_here - 1) * a.ldx) + ((Hc + 7) & ~7)) * 2;
+
+    uint32_t wvo[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        wvo[r] = (uint32_t)(((int64_t)(8 * g + r) * a.ldw + 8 * n) * 2);
+    uint32_t xvo[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+        xvo[mb] = (uint32_t)(((int64_t)(kRowBlock * mb + n) * a.ldx + 8 * g) * 2);
+
+    f32x4 acc[MB][8];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            acc[mb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // this wave's steps wave, wave + 4, ... of the chunk, in pairs
+    const int nsteps = (Hc + kStepK - 1) / kStepK;
+    const int nw = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;
+    constexpr int kStride = kWaves * kStepK;
+    Frags<MB> fa, fb;
+    if (nw > 0)
+        load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, wave * kStepK, a.ldw, wvo, xvo);
+    int k0 = wave * kStepK;
+    for (int i = 0; i + 2 <= nw; i += 2) {
+        load_step<MB, POL>(fb, wbase, wbytes, xbase, xbytes, k0 + kStride, a.ldw, wvo, xvo);
+        compute_step<MB>(fa, acc, k0, Hc, g);
+        if (i + 2 < nw)
+            load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, k0 + 2 * kStride, a.ldw, wvo,
+                               xvo);
+        compute_step<MB>(fb, acc, k0 + kStride, Hc, g);
+        k0 += 2 * kStride;
+    }
+    if (nw & 1)
+        compute_step<MB>(fa, acc, k0, Hc, g);
+
+    // fold the four wave partials (wave order) and store the chunk partial
+    const int erow = threadIdx.x >> 4;
+    const int cg = threadIdx.x & 15;
+    const int col = c0 + 8 * cg;
+    const int nvalid = max(0, min(8, a.N - col));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        if (m0 + kRowBlock * mb >= a.B)
+            break;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const f32x4 lo = {acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+            const f32x4 hi = {acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
+            *reinterpret_cast<f32x4 *>(&red[wave][4 * g + r][8 * n]) = lo;
+            *reinterpret_cast<f32x4 *>(&red[wave][4 * g + r][8 * n + 4]) = hi;
+        }
+        __syncthreads();
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            y[j] = ((red[0][erow][8 * cg + j] + red[1][erow][8 * cg + j]) +
+                    red[2][erow][8 * cg + j]) + red[3][erow][8 * cg + j];
+        __syncthreads();
+        const int b = m0 + kRowBlock * mb + erow;
+        if (b < a.B) {
+            float *dst = a.part + ((int64_t)chunk * a.B + b) * a.ldp + col;
+            if (nvalid == 8) {
+                *reinterpret_cast<f32x4 *>(dst) = f32x4{y[0], y[1], y[2], y[3]};
+                *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{y[4], y[5], y[6], y[7]};
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (j < nvalid)
+                        dst[j] = y[j];
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ f32x4 reduce_op(int op, f32x4 a, f32x4 b)
+{
+    switch (op) {
+    case kRedSum:
+        return a + b;
+    case kRedProd:
+        return a * b;
+    case kRedMin:
+        return f32x4{fminf(a[0], b[0]), fminf(a[1], b[1]), fminf(a[2], b[2]), fminf(a[3], b[3])};
+    default:
+        return f32x4{fmaxf(a[0], b[0]), fmaxf(a[1], b[1]), fmaxf(a[2], b[2]), fmaxf(a[3], b[3])};
+    }
+}
+
+// One thread per (row, 4 columns): the lane's chunk partials summed in
+// ascending chunk order, the lanes folded with the operator in ascending
+// lane order.  ldp is a multiple of 4, so a thread's 4 partial columns are
+// one aligned vector (columns past N are never stored).
+__global__ __launch_bounds__(kThreads) void partial_reduce_kernel(const PartialArgs a, int op,
+                                                                  float *out, int64_t ldo)
+{
+    const int b = blockIdx.y;
+    const int col = (blockIdx.x * kThreads + threadIdx.x) * 4;
+    if (col >= a.N)
+        return;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int lane = 0; lane < a.k; ++lane) {
+        f32x4 q = {0.f, 0.f, 0.f, 0.f};
+        for (int c = a.chunk0[lane]; c < a.chunk0[lane + 1]; ++c)
+            q += *reinterpret_cast<const f32x4 *>(a.part + ((int64_t)c * a.B + b) * a.ldp + col);
+        acc = lane == 0 ? q : reduce_op(op, acc, q);
+    }
+    float *dst = out + (int64_t)b * ldo + col;
+    if (col + 4 <= a.N) {
+        *reinterpret_cast<f32x4 *>(dst) = acc;
+    } else {
+        for (int j = 0; j < 4 && col + j < a.N; ++j)
+            dst[j] = acc[j];
+    }
+}
+
+template <int MB, int POL>
+hipError_t launch_partial_mb(const PartialArgs &a, hipStream_t s)
+{
+    const int groups = (a.B + kRowBlock * MB - 1) / (kRowBlock * MB);
+    const int64_t nwg = (int64_t)a.chunk0[a.k] * a.T * groups;
+    hipLaunchKernelGGL((partial_gemm_kernel<MB, POL>), dim3((unsigned)nwg), dim3(kThreads), 0, s,
+                       a);
+    return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s)
@@ -1184,6 +1363,35 @@ hipError_t launch_row_argmax(const float *logits, int64_t ldl, int32_t B, int32_
     one.tile0[0] = 0;
     one.tile0[1] = nchunks;
     return launch_combine(partial, nullptr, one, B, nchunks, ids, nullptr, nullptr, s);
+}
+
+hipError_t launch_partial_gemm(const PartialArgs &a, hipStream_t s)
+{
+    if (a.B <= 0 || a.chunk0[a.k] <= 0)
+        return hipSuccess;
+    // one row group: every weight byte is read once, so stream it
+    switch (rows_per_group(a.B) / kRowBlock) {
+    case 1:
+        return launch_partial_mb<1, kPolicyStream>(a, s);
+    case 2:
+        return launch_partial_mb<2, kPolicyStream>(a, s);
+    default:
+        if (a.B <= kRowBlock * kMaxMB)
+            return launch_partial_mb<kMaxMB, kPolicyStream>(a, s);
+        return launch_partial_mb<kMaxMB, kPolicyShared>(a, s);
+    }
+}
+
+hipError_t launch_partial_reduce(const PartialArgs &a, int op, float *out, int64_t ldo,
+                                 hipStream_t s)
+{
+    if (a.B <= 0)
+        return hipSuccess;
+    if (op < kRedSum || op > kRedMax)
+        return hipErrorInvalidValue;
+    dim3 grid((a.N + 4 * kThreads - 1) / (4 * kThreads), a.B);
+    hipLaunchKernelGGL(partial_reduce_kernel, grid, dim3(kThreads), 0, s, a, op, out, ldo);
+    return hipGetLastError();
 }
 
 }  // namespace sbk

@@ -199,6 +199,63 @@ T *region(void *ws, size_t off)
     return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
+// ---------------------------------------------------------------------------
+// Partial completion
+// ---------------------------------------------------------------------------
+sb_status check_partial(const sb_partial_desc *d)
+{
+    if (!d || !d->lane_k || !d->x || !d->w)
+        return SB_ERR_NULL;
+    if (d->B < 0 || d->N < 1)
+        return SB_ERR_SHAPE;
+    if (d->k < 1 || d->k > SB_MAX_LANES || d->lane_k[0] != 0)
+        return SB_ERR_LANES;
+    int64_t maxk = 0;
+    for (int i = 0; i < d->k; ++i) {
+        if (d->lane_k[i + 1] <= d->lane_k[i])
+            return SB_ERR_LANES;
+        const int64_t ki = (int64_t)d->lane_k[i + 1] - d->lane_k[i];
+        if (ki > maxk)
+            maxk = ki;
+    }
+    if (d->B > 0)
+        for (int i = 0; i < d->k; ++i)
+            if (!d->x[i] || !d->w[i])
+                return SB_ERR_NULL;
+    if (d->ldx < maxk || d->ldw < d->N)
+        return SB_ERR_SHAPE;
+    if (d->B > 0) {
+        if ((d->ldx % 8) != 0 || (d->ldw % 8) != 0)
+            return SB_ERR_ALIGN;
+        for (int i = 0; i < d->k; ++i)
+            if (!aligned16(d->x[i]) || !aligned16(d->w[i]))
+                return SB_ERR_ALIGN;
+    }
+    if (d->B > kMaxRows)
+        return SB_ERR_UNSUPPORTED;
+    // per-chunk buffer offsets are 32-bit: a chunk of weight rows and one row
+    // group of an activation shard must span less than 4 GiB
+    if ((int64_t)(sbk::kPartChunk + 8) * d->ldw * 2 >= ((int64_t)1 << 32) ||
+        (int64_t)(sbk::kRowBlock * sbk::kMaxMB) * d->ldx * 2 >= ((int64_t)1 << 32))
+        return SB_ERR_UNSUPPORTED;
+    return SB_OK;
+}
+
+int partial_chunks(const sb_partial_desc *d)
+{
+    int n = 0;
+    for (int i = 0; i < d->k; ++i)
+        n += (d->lane_k[i + 1] - d->lane_k[i] + sbk::kPartChunk - 1) / sbk::kPartChunk;
+    return n;
+}
+
+size_t partial_bytes(const sb_partial_desc *d)
+{
+    return align_up((size_t)partial_chunks(d) * (size_t)d->B * (size_t)shard_ld(d->N) *
+                        sizeof(float),
+                    kRegionAlign);
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,6 +386,63 @@ sb_status sb_full_logits(const sb_head_desc *desc, float *logits, int64_t ldl, i
         return SB_ERR_HIP;
     if (ids && sbk::launch_row_argmax(logits, ldl, a.B, a.V, region<int2>(ws, L.partial), ids,
                                       s) != hipSuccess)
+        return SB_ERR_HIP;
+    return SB_OK;
+}
+
+size_t sb_partial_workspace_bytes(const sb_partial_desc *desc, sb_status *status)
+{
+    const sb_status st = check_partial(desc);
+    if (status)
+        *status = st;
+    return st == SB_OK ? partial_bytes(desc) : 0;
+}
+
+sb_status sb_partial_complete(const sb_partial_desc *desc, int op, float *out, int64_t ldo,
+                              void *ws, size_t ws_bytes, void *stream)
+{
+    sb_status st = check_partial(desc);
+    if (st != SB_OK)
+        return st;
+    if (op < SB_RED_SUM || op > SB_RED_MAX)
+        return SB_ERR_SHAPE;
+    if (desc->B == 0)
+        return SB_OK;
+    if (!out)
+        return SB_ERR_NULL;
+    if (ldo < desc->N)
+        return SB_ERR_SHAPE;
+    if (!aligned16(out) || (ldo % 4) != 0)
+        return SB_ERR_ALIGN;
+    const size_t need = partial_bytes(desc);
+    if (!ws)
+        return SB_ERR_NULL;
+    if (ws_bytes < need)
+        return SB_ERR_WORKSPACE;
+    if (!aligned16(ws))
+        return SB_ERR_ALIGN;
+    sbk::PartialArgs a;
+    memset(&a, 0, sizeof a);
+    a.k = desc->k;
+    int chunks = 0;
+    for (int i = 0; i < desc->k; ++i) {
+        a.x[i] = static_cast<const uint16_t *>(desc->x[i]);
+        a.w[i] = static_cast<const uint16_t *>(desc->w[i]);
+        a.K[i] = desc->lane_k[i + 1] - desc->lane_k[i];
+        a.chunk0[i] = chunks;
+        chunks += (a.K[i] + sbk::kPartChunk - 1) / sbk::kPartChunk;
+    }
+    a.chunk0[desc->k] = chunks;
+    a.ldx = desc->ldx;
+    a.ldw = desc->ldw;
+    a.B = desc->B;
+    a.N = desc->N;
+    a.T = (desc->N + sbk::kTileN - 1) / sbk::kTileN;
+    a.part = static_cast<float *>(ws);
+    a.ldp = shard_ld(desc->N);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (sbk::launch_partial_gemm(a, s) != hipSuccess ||
+        sbk::launch_partial_reduce(a, op, out, ldo, s) != hipSuccess)
         return SB_ERR_HIP;
     return SB_OK;
 }

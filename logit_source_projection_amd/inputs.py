@@ -204,3 +204,40 @@ def make_random(B, H, V, lane_off, seed=0, sigma_x=1.0, sigma_w=0.02):
     w = draw_weight(H, V, sigma_w, seed)
     return dict(name="random", x=x, w=w, lane_off=list(lane_off), B=B, H=H,
                 V=V, k=len(lane_off) - 1, planted=[])
+
+
+# --------------------------------------------------------------------------
+# Partial-completion workloads (the row-parallel MLP down projection of the
+# pages' Qwen3-14B layer: 17408 intermediate columns in two lanes of 8704,
+# hidden size 5120; SemBridge section 6.4).  Lane i's activation shard is
+# drawn from rng [seed, 2, i] and its weight rows from rng [seed, 3, i, c].
+# --------------------------------------------------------------------------
+
+PARTIAL_WORKLOADS = {
+    # name: (B, N, K per lane, sigma_w)
+    "mlp_down": (16, 5120, (8704, 8704), 0.02),
+}
+
+
+def draw_partial(B, N, Ks, seed=0, sigma_x=1.0, sigma_w=0.02):
+    """Activation shards xs[i] (uint16 [B, K_i]) and weight blocks ws[i]
+    (uint16 [K_i, N]) of a partial-completion boundary."""
+    xs, ws = [], []
+    for i, K in enumerate(Ks):
+        rx = np.random.default_rng([seed, 2, i])
+        xs.append(f32_to_bf16_bits(rx.standard_normal((B, K), dtype=np.float32) * sigma_x))
+        rows = []
+        for c in range(0, K, 256):
+            rw = np.random.default_rng([seed, 3, i, c // 256])
+            rows.append(f32_to_bf16_bits(
+                rw.standard_normal((min(256, K - c), N), dtype=np.float32) * sigma_w))
+        ws.append(np.concatenate(rows, axis=0))
+    return xs, ws
+
+
+def make_partial(name, seed=0, B=None):
+    """Inputs of a named partial-completion workload: dict(xs, ws, B, N, Ks)."""
+    B0, N, Ks, sw = PARTIAL_WORKLOADS[name]
+    B = B0 if B is None else int(B)
+    xs, ws = draw_partial(B, N, Ks, seed, sigma_w=sw)
+    return dict(name=name, xs=xs, ws=ws, B=B, N=N, Ks=list(Ks))

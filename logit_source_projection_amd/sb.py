@@ -30,8 +30,15 @@ SB_SURF_FULL_LOGITS = 3
 
 SB_MAX_LANES = 64
 
+SB_RED_SUM = 0
+SB_RED_PROD = 1
+SB_RED_MIN = 2
+SB_RED_MAX = 3
+REDUCE_OPS = {"sum": SB_RED_SUM, "prod": SB_RED_PROD, "min": SB_RED_MIN, "max": SB_RED_MAX}
+
 EXPORTS = ("sb_workspace_bytes", "sb_project_tokens", "sb_project_logprobs",
-           "sb_full_logits", "sb_status_string")
+           "sb_full_logits", "sb_partial_workspace_bytes", "sb_partial_complete",
+           "sb_status_string")
 
 
 class SbError(RuntimeError):
@@ -46,6 +53,15 @@ class sb_head_desc(ctypes.Structure):
         ("V", ctypes.c_int32), ("k", ctypes.c_int32),
         ("lane_off", ctypes.POINTER(ctypes.c_int32)),
         ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
+        ("w", ctypes.POINTER(ctypes.c_void_p)), ("ldw", ctypes.c_int64),
+    ]
+
+
+class sb_partial_desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("N", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("lane_k", ctypes.POINTER(ctypes.c_int32)),
+        ("x", ctypes.POINTER(ctypes.c_void_p)), ("ldx", ctypes.c_int64),
         ("w", ctypes.POINTER(ctypes.c_void_p)), ("ldw", ctypes.c_int64),
     ]
 
@@ -73,6 +89,11 @@ def lib():
     L.sb_project_logprobs.argtypes = [P, vp, vp, vp, vp, i64, vp, sz, vp]
     L.sb_full_logits.restype = ctypes.c_int
     L.sb_full_logits.argtypes = [P, vp, i64, vp, vp, sz, vp]
+    PP = ctypes.POINTER(sb_partial_desc)
+    L.sb_partial_workspace_bytes.restype = sz
+    L.sb_partial_workspace_bytes.argtypes = [PP, ctypes.POINTER(ctypes.c_int)]
+    L.sb_partial_complete.restype = ctypes.c_int
+    L.sb_partial_complete.argtypes = [PP, ctypes.c_int, vp, i64, vp, sz, vp]
     L.sb_status_string.restype = ctypes.c_char_p
     L.sb_status_string.argtypes = [ctypes.c_int]
     _lib = L
@@ -200,6 +221,68 @@ def sb_full_logits(head, logits, ids=None, ws=None, stream=None):
     _check(lib().sb_full_logits(head.ref(), _ptr(logits), logits.stride(0), _ptr(ids),
                                 _ptr(ws), ws.numel(), _stream(stream)), "sb_full_logits")
     return logits
+
+
+class Partial:
+    """Descriptor of a row-parallel partial-completion boundary: k activation
+    shards x[i] [B, K_i] (bf16, one common row stride) and weight blocks
+    w[i] [K_i, N] (bf16, one common row stride).  Raw values can be
+    overridden to exercise the ABI's validation."""
+
+    def __init__(self, x, w, *, B=None, N=None, lane_k=None, ldx=None, ldw=None,
+                 x_ptrs=None, w_ptrs=None):
+        self.x, self.w = list(x), list(w)
+        Ks = [t.shape[1] for t in self.x]
+        off = [0]
+        for kk in Ks:
+            off.append(off[-1] + kk)
+        if lane_k is not None:
+            off = [int(o) for o in lane_k]
+        k = len(off) - 1
+        self._off = (ctypes.c_int32 * max(1, k + 1))(*off)
+        xp = [t.data_ptr() for t in self.x] if x_ptrs is None else list(x_ptrs)
+        wp = [t.data_ptr() for t in self.w] if w_ptrs is None else list(w_ptrs)
+        self._x = (ctypes.c_void_p * max(1, len(xp)))(*xp)
+        self._w = (ctypes.c_void_p * max(1, len(wp)))(*wp)
+        self.desc = sb_partial_desc(
+            B=self.x[0].shape[0] if B is None else B,
+            N=self.w[0].shape[1] if N is None else N,
+            k=k, lane_k=self._off, x=self._x,
+            ldx=self.x[0].stride(0) if ldx is None else ldx,
+            w=self._w,
+            ldw=self.w[0].stride(0) if ldw is None else ldw)
+
+    @property
+    def B(self):
+        return self.desc.B
+
+    @property
+    def N(self):
+        return self.desc.N
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def sb_partial_workspace_bytes(part):
+    st = ctypes.c_int(0)
+    n = lib().sb_partial_workspace_bytes(part.ref(), ctypes.byref(st))
+    if st.value != SB_OK:
+        raise SbError(st.value, "sb_partial_workspace_bytes")
+    return int(n)
+
+
+def sb_partial_complete(part, op, out, ws=None, stream=None):
+    """out (fp32 [B, N], row stride out.stride(0)) <- the registered
+    reduction `op` ("sum", "prod", "min", "max" or an SB_RED_* code) of the
+    lane partials."""
+    code = REDUCE_OPS[op] if isinstance(op, str) else int(op)
+    if ws is None:
+        ws = torch.empty(max(sb_partial_workspace_bytes(part), 16), dtype=torch.uint8,
+                         device=out.device)
+    _check(lib().sb_partial_complete(part.ref(), code, _ptr(out), out.stride(0), _ptr(ws),
+                                     ws.numel(), _stream(stream)), "sb_partial_complete")
+    return out
 
 
 def to_device_bf16(bits, device="cuda"):

@@ -157,3 +157,73 @@ def test_binding_raises_on_error():
     with pytest.raises(sb.SbError) as e:
         sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS)
     assert e.value.status == sb.SB_ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# partial completion
+# ---------------------------------------------------------------------------
+def fake_partial(B=16, N=5120, lane_k=(0, 8704, 17408), ldx=None, ldw=None,
+                 x_ptrs=None, w_ptrs=None):
+    k = len(lane_k) - 1
+    Ks = [lane_k[i + 1] - lane_k[i] for i in range(k)]
+    return sb.Partial([torch.empty(0, 1)] * k, [torch.empty(0, 1)] * k, B=B, N=N,
+                      lane_k=list(lane_k), ldx=max(Ks) if ldx is None else ldx,
+                      ldw=N if ldw is None else ldw,
+                      x_ptrs=[FAKE] * k if x_ptrs is None else x_ptrs,
+                      w_ptrs=[FAKE] * k if w_ptrs is None else w_ptrs)
+
+
+def partial_status(p, op=sb.SB_RED_SUM, out=FAKE, ldo=None, ws=FAKE, ws_bytes=1 << 30):
+    return sb.lib().sb_partial_complete(p.ref(), op, out, p.N if ldo is None else ldo, ws,
+                                        ws_bytes, None)
+
+
+def test_partial_workspace_bytes():
+    # two lanes of 8704 rows -> 17 + 17 chunks of 512 rows, fp32 [B][N] each
+    p = fake_partial()
+    assert sb.sb_partial_workspace_bytes(p) == 34 * 16 * 5120 * 4
+    # ragged: 1000 rows -> 2 chunks; N = 130 -> row stride 132
+    p = fake_partial(B=3, N=130, lane_k=(0, 1000), ldw=136)
+    assert sb.sb_partial_workspace_bytes(p) == (2 * 3 * 132 * 4 + 255) // 256 * 256
+    assert sb.sb_partial_workspace_bytes(fake_partial(B=0)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), sb.SB_ERR_SHAPE),
+    (dict(N=0, ldw=8), sb.SB_ERR_SHAPE),
+    (dict(lane_k=(0, 100, 100)), sb.SB_ERR_LANES),
+    (dict(lane_k=(8, 100)), sb.SB_ERR_LANES),
+    (dict(lane_k=tuple(range(0, 8 * 66, 8))), sb.SB_ERR_LANES),
+    (dict(ldx=8000), sb.SB_ERR_SHAPE),
+    (dict(ldw=5000), sb.SB_ERR_SHAPE),
+    (dict(ldx=8708), sb.SB_ERR_ALIGN),
+    (dict(ldw=5124), sb.SB_ERR_ALIGN),
+    (dict(x_ptrs=[FAKE, FAKE + 8]), sb.SB_ERR_ALIGN),
+    (dict(w_ptrs=[FAKE + 2, FAKE]), sb.SB_ERR_ALIGN),
+    (dict(x_ptrs=[FAKE, 0]), sb.SB_ERR_NULL),
+    (dict(w_ptrs=[0, FAKE]), sb.SB_ERR_NULL),
+    (dict(B=65536), sb.SB_ERR_UNSUPPORTED),
+    (dict(ldw=1 << 22), sb.SB_ERR_UNSUPPORTED),  # a 512-row chunk spans 4 GiB
+])
+def test_partial_descriptor_validation(kw, status):
+    p = fake_partial(**kw)
+    st = ctypes.c_int(123)
+    sb.lib().sb_partial_workspace_bytes(p.ref(), ctypes.byref(st))
+    assert st.value == status
+    assert partial_status(p) == status
+
+
+def test_partial_output_and_workspace_checks():
+    p = fake_partial()
+    need = sb.sb_partial_workspace_bytes(p)
+    assert partial_status(p, op=4) == sb.SB_ERR_SHAPE
+    assert partial_status(p, op=-1) == sb.SB_ERR_SHAPE
+    assert partial_status(p, out=None) == sb.SB_ERR_NULL
+    assert partial_status(p, ldo=5119) == sb.SB_ERR_SHAPE
+    assert partial_status(p, ldo=5122) == sb.SB_ERR_ALIGN
+    assert partial_status(p, out=FAKE + 8) == sb.SB_ERR_ALIGN
+    assert partial_status(p, ws=None) == sb.SB_ERR_NULL
+    assert partial_status(p, ws_bytes=need - 1) == sb.SB_ERR_WORKSPACE
+    assert partial_status(p, ws=FAKE + 4) == sb.SB_ERR_ALIGN
+    # an empty batch is a valid no-op that touches nothing
+    assert partial_status(fake_partial(B=0), out=None, ws=None, ws_bytes=0) == sb.SB_OK
