@@ -30,7 +30,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dense_decode",
-                    choices=["tiny", "dense_decode", "moe_decode", "large_vocab", "prefill"])
+                    choices=["tiny", "dense_decode", "moe_decode", "large_vocab", "prefill",
+                             "mlp_down"],
+                    help="mlp_down times sb_partial_complete (the row-parallel MLP down "
+                         "projection) instead of the head")
+    ap.add_argument("--op", default="sum", choices=["sum", "prod", "min", "max"],
+                    help="registered reduction of the mlp_down workload")
     ap.add_argument("--B", type=int, default=None, help="row count override (large_vocab sweep)")
     ap.add_argument("--surface", default=None,
                     choices=["tokens", "logprobs", "logprobs_full", "full_logits"],
@@ -291,8 +296,87 @@ def cpu_baseline(d):
                        f"{dt:.2f} s"), r, rows
 
 
+def bench_partial(args):
+    """The partial-completion call on the Qwen3-14B-shaped down projection:
+    inputs resident in HBM, warm-up calls, then K calls timed with HIP events
+    on the launch stream; the oracle timed beside it on the host."""
+    import numpy as np
+    import torch
+    from logit_source_projection_amd import inputs, sb
+    import oracle.partial as opart
+
+    d = inputs.make_partial(args.workload, B=args.B)
+    B, N, Ks = d["B"], d["N"], d["Ks"]
+    dev = torch.device("cuda:0")
+    ldx = (max(Ks) + 7) // 8 * 8
+    xs = []
+    for x in d["xs"]:
+        xp = np.zeros((B, ldx), dtype=np.uint16)
+        xp[:, :x.shape[1]] = x
+        xs.append(sb.to_device_bf16(xp, dev)[:, :x.shape[1]])
+    ws = [sb.to_device_bf16(w, dev) for w in d["ws"]]
+    part = sb.Partial(xs, ws)
+    out = torch.empty(B, (N + 3) // 4 * 4, dtype=torch.float32, device=dev)[:, :N]
+    wsp = torch.empty(max(sb.sb_partial_workspace_bytes(part), 16), dtype=torch.uint8,
+                      device=dev)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def call():
+        sb.sb_partial_complete(part, args.op, out, ws=wsp, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        call()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = sum(K * N * 2 for K in Ks) + sum(B * K * 2 for K in Ks) + B * N * 4
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "partial-completion rows/s (row-parallel down projection); % HBM roofline",
+        "value": B / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "N": N, "K": Ks, "op": args.op},
+        "roofline": dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                         unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                         kernel="whole call (chunked partial GEMM and the lane reduction)",
+                         algorithmic_bytes=nbytes),
+        "cpu_baseline": None, "report": {},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        passes = 0
+        while passes == 0 or time.perf_counter() - t0 < CPU_SECONDS:
+            ref = opart.partial_complete(d["xs"], d["ws"], args.op)
+            passes += 1
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = dict(
+            value=B * passes / dt, unit="rows/s", cores=oracle.max_threads(), kind="oracle",
+            sample=f"all {B} rows of the workload, {passes} passes (fp64 partials + "
+                   f"{args.op} over the lanes), {dt:.2f} s")
+        g = out.cpu().numpy().astype(np.float64)
+        scale = np.abs(ref).max(axis=1)
+        line["report"]["max_row_rel_err_vs_oracle"] = float(
+            (np.abs(g - ref).max(axis=1) / np.maximum(scale, 1e-30)).max())
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
+    if args.workload == "mlp_down" and not args.record_traffic:
+        world = int(os.environ.get("WORLD_SIZE", "1"))
+        if args.gpus != 1 or world != 1:
+            print("bench.py measures one GPU only.", file=sys.stderr)
+            sys.exit(2)
+        bench_partial(args)
+        return
     if args.surface is None:
         args.surface = "logprobs_full" if args.workload == "prefill" else "tokens"
     if args.record_traffic:

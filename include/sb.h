@@ -181,7 +181,7 @@ sb_status sb_full_logits(const sb_head_desc *desc, float *logits, int64_t ldl,
  * registered elementwise operator completes the partials before the output
  * is exposed:  out = op(...op(op(P_0, P_1), P_2)..., P_{k-1})  (ascending
  * lane order).  Each P_i is accumulated in an order fixed by the shapes
- * alone (512-row chunks summed in ascending order), so repeated calls give
+ * alone (1024-row chunks summed in a fixed order), so repeated calls give
  * bit-identical outputs.
  * ---------------------------------------------------------------------------
  */

@@ -115,7 +115,7 @@ hipError_t launch_row_argmax(const float *logits, int64_t ldl, int32_t B, int32_
 // matching weight rows W_i [K_i][N]; its partial is P_i = X_i . W_i, and a
 // registered elementwise operator completes the k partials in lane order.
 // ---------------------------------------------------------------------------
-constexpr int kPartChunk = 512;  // reduction rows per workgroup (split K)
+constexpr int kPartChunk = 1024;  // reduction rows per workgroup (split K)
 
 enum ReduceOp : int { kRedSum = 0, kRedProd = 1, kRedMin = 2, kRedMax = 3 };
 
@@ -123,7 +123,7 @@ struct PartialArgs {
     const uint16_t *x[kMaxLanes];   // lane i's activation shard, bf16 [B][ldx]
     const uint16_t *w[kMaxLanes];   // lane i's weight rows, bf16 [K_i][ldw]
     int32_t K[kMaxLanes];           // reduction rows of lane i
-    int32_t chunk0[kMaxLanes + 1];  // first chunk of lane i (prefix sums of ceil(K_i / 512))
+    int32_t chunk0[kMaxLanes + 1];  // first chunk of lane i (prefix sums of ceil(K_i / kPartChunk))
     int64_t ldx, ldw;
     int32_t B, N, k;
     int32_t T;                      // 128-column tiles of the output

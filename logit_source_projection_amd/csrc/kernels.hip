@@ -1101,7 +1101,7 @@ hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
 //
 // The output is only N columns wide (N / 128 tiles), so the reduction
 // dimension is split as well: one workgroup computes a 128-column tile of
-// one 512-row chunk of one lane for 16*MB rows, with the head kernel's
+// one kPartChunk-row chunk of one lane for 16*MB rows, with the head kernel's
 // mainloop (4 waves, K steps interleaved over the waves, wave-order fold
 // through LDS), and stores the chunk partial in fp32.  The reduce kernel then
 // sums a lane's chunks in ascending order and folds the lanes with the
@@ -1238,30 +1238,59 @@ __device__ __forceinline__ f32x4 reduce_op(int op, f32x4 a, f32x4 b)
     }
 }
 
-// One thread per (row, 4 columns): the lane's chunk partials summed in
-// ascending chunk order, the lanes folded with the operator in ascending
-// lane order.  ldp is a multiple of 4, so a thread's 4 partial columns are
-// one aligned vector (columns past N are never stored).
+// A workgroup covers kRedCols columns of one row: thread (q, j) takes column
+// quad q and, of every lane, the chunks j, j + 4, ... (ascending); the four
+// part sums of a lane are added in the fixed order ((s0 + s1) + s2) + s3
+// through LDS, and the lanes are folded with the operator in ascending lane
+// order.  ldp is a multiple of 4, so a quad is one aligned vector (columns
+// past N are never stored).
+constexpr int kRedSplit = 4;
+constexpr int kRedCols = kThreads / kRedSplit * 4;
+
 __global__ __launch_bounds__(kThreads) void partial_reduce_kernel(const PartialArgs a, int op,
                                                                   float *out, int64_t ldo)
 {
+    __shared__ f32x4 sums[kRedSplit][kThreads / kRedSplit];
     const int b = blockIdx.y;
-    const int col = (blockIdx.x * kThreads + threadIdx.x) * 4;
-    if (col >= a.N)
-        return;
+    const int q = threadIdx.x % (kThreads / kRedSplit);
+    const int j = threadIdx.x / (kThreads / kRedSplit);
+    const int col = blockIdx.x * kRedCols + 4 * q;
+    const bool colok = col < a.N;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int lane = 0; lane < a.k; ++lane) {
-        f32x4 q = {0.f, 0.f, 0.f, 0.f};
-        for (int c = a.chunk0[lane]; c < a.chunk0[lane + 1]; ++c)
-            q += *reinterpret_cast<const f32x4 *>(a.part + ((int64_t)c * a.B + b) * a.ldp + col);
-        acc = lane == 0 ? q : reduce_op(op, acc, q);
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        if (colok) {
+            const float *p = a.part + ((int64_t)a.chunk0[lane] * a.B + b) * a.ldp + col;
+            const int64_t stride = (int64_t)a.B * a.ldp;
+            const int nc = a.chunk0[lane + 1] - a.chunk0[lane];
+            int c = j;
+            // four independent loads in flight, added in ascending chunk order
+            for (; c + 3 * kRedSplit < nc; c += 4 * kRedSplit) {
+                const f32x4 v0 = *reinterpret_cast<const f32x4 *>(p + c * stride);
+                const f32x4 v1 = *reinterpret_cast<const f32x4 *>(p + (c + kRedSplit) * stride);
+                const f32x4 v2 = *reinterpret_cast<const f32x4 *>(p + (c + 2 * kRedSplit) * stride);
+                const f32x4 v3 = *reinterpret_cast<const f32x4 *>(p + (c + 3 * kRedSplit) * stride);
+                s = (((s + v0) + v1) + v2) + v3;
+            }
+            for (; c < nc; c += kRedSplit)
+                s += *reinterpret_cast<const f32x4 *>(p + c * stride);
+        }
+        sums[j][q] = s;
+        __syncthreads();
+        if (j == 0) {
+            const f32x4 t = ((sums[0][q] + sums[1][q]) + sums[2][q]) + sums[3][q];
+            acc = lane == 0 ? t : reduce_op(op, acc, t);
+        }
+        __syncthreads();
     }
+    if (j != 0 || !colok)
+        return;
     float *dst = out + (int64_t)b * ldo + col;
     if (col + 4 <= a.N) {
         *reinterpret_cast<f32x4 *>(dst) = acc;
     } else {
-        for (int j = 0; j < 4 && col + j < a.N; ++j)
-            dst[j] = acc[j];
+        for (int e = 0; e < 4 && col + e < a.N; ++e)
+            dst[e] = acc[e];
     }
 }
 
@@ -1389,7 +1418,7 @@ hipError_t launch_partial_reduce(const PartialArgs &a, int op, float *out, int64
         return hipSuccess;
     if (op < kRedSum || op > kRedMax)
         return hipErrorInvalidValue;
-    dim3 grid((a.N + 4 * kThreads - 1) / (4 * kThreads), a.B);
+    dim3 grid((a.N + kRedCols - 1) / kRedCols, a.B);
     hipLaunchKernelGGL(partial_reduce_kernel, grid, dim3(kThreads), 0, s, a, op, out, ldo);
     return hipGetLastError();
 }

@@ -179,12 +179,12 @@ def partial_status(p, op=sb.SB_RED_SUM, out=FAKE, ldo=None, ws=FAKE, ws_bytes=1 
 
 
 def test_partial_workspace_bytes():
-    # two lanes of 8704 rows -> 17 + 17 chunks of 512 rows, fp32 [B][N] each
+    # two lanes of 8704 rows -> 9 + 9 chunks of 1024 rows, fp32 [B][N] each
     p = fake_partial()
-    assert sb.sb_partial_workspace_bytes(p) == 34 * 16 * 5120 * 4
-    # ragged: 1000 rows -> 2 chunks; N = 130 -> row stride 132
-    p = fake_partial(B=3, N=130, lane_k=(0, 1000), ldw=136)
-    assert sb.sb_partial_workspace_bytes(p) == (2 * 3 * 132 * 4 + 255) // 256 * 256
+    assert sb.sb_partial_workspace_bytes(p) == 18 * 16 * 5120 * 4
+    # ragged: 1000 + 1025 rows -> 1 + 2 chunks; N = 130 -> row stride 132
+    p = fake_partial(B=3, N=130, lane_k=(0, 1000, 2025), ldx=1032, ldw=136)
+    assert sb.sb_partial_workspace_bytes(p) == (3 * 3 * 132 * 4 + 255) // 256 * 256
     assert sb.sb_partial_workspace_bytes(fake_partial(B=0)) == 0
 
 
@@ -203,7 +203,7 @@ def test_partial_workspace_bytes():
     (dict(x_ptrs=[FAKE, 0]), sb.SB_ERR_NULL),
     (dict(w_ptrs=[0, FAKE]), sb.SB_ERR_NULL),
     (dict(B=65536), sb.SB_ERR_UNSUPPORTED),
-    (dict(ldw=1 << 22), sb.SB_ERR_UNSUPPORTED),  # a 512-row chunk spans 4 GiB
+    (dict(ldw=1 << 21), sb.SB_ERR_UNSUPPORTED),  # a 1024-row chunk spans 4 GiB
 ])
 def test_partial_descriptor_validation(kw, status):
     p = fake_partial(**kw)
