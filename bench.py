@@ -120,10 +120,15 @@ def _counter_per_dispatch(csv_path):
 
 
 def record_traffic(args):
-    """Scale the head kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by
-    what the same counters read for the plain copy of known size run in the
-    same process, and store the bytes per launch in the traffic file."""
+    """Scale the call's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the
+    same counters read for the plain copy of known size run in the same
+    process, and store the bytes per call in the traffic file.  A head call
+    below 256 rows is one head_gemm_kernel launch; the partial-completion
+    call is the partial GEMM plus the lane reduction, whose per-dispatch
+    averages are added."""
     from logit_source_projection_amd import inputs
+    kernel_tags = ("partial_gemm", "partial_reduce") if args.workload == "mlp_down" \
+        else ("head_gemm",)
     calib = args.copy_calibration_mib << 20
     if calib <= 0:
         sys.exit("--record-traffic needs the --copy-calibration-mib of the profiled run")
@@ -133,19 +138,27 @@ def record_traffic(args):
         # the calibration copy is the largest copy dispatch (small uploads
         # of the inputs may be copies too)
         copy = sorted(v for k, vs in per.items() if "copyBuffer" in k for v in vs)[-1:]
-        heads = {k: vs for k, vs in per.items() if "head_gemm" in k}
-        if not copy or not heads:
-            sys.exit(f"{path}: expected a copy dispatch and head kernel dispatches")
-        name, vals = max(heads.items(), key=lambda kv: len(kv[1]))
+        names, kib, ndisp = [], 0.0, 0
+        for tag in kernel_tags:
+            found = {k: vs for k, vs in per.items() if tag in k}
+            if not found:
+                sys.exit(f"{path}: no dispatch of {tag}")
+            name, vals = max(found.items(), key=lambda kv: len(kv[1]))
+            names.append(name)
+            kib += sum(vals) / len(vals)
+            ndisp = len(vals)
+        if not copy:
+            sys.exit(f"{path}: expected a copy dispatch")
         factor = calib / (copy[0] * 1024.0)
-        kib = sum(vals) / len(vals)
-        rec[which] = dict(kernel=name, dispatches=len(vals), kib_per_dispatch=round(kib, 3),
-                          copy_kib=copy[0], factor=round(factor, 5),
-                          bytes=int(round(kib * 1024.0 * factor)))
+        rec[which] = dict(kernel=" + ".join(names), dispatches=ndisp,
+                          kib_per_dispatch=round(kib, 3), copy_kib=copy[0],
+                          factor=round(factor, 5), bytes=int(round(kib * 1024.0 * factor)))
     if rec["fetch"]["kernel"] != rec["write"]["kernel"]:
         sys.exit("the two passes name different head kernels")
-    d = inputs.WORKLOADS[args.workload]
+    d = (inputs.PARTIAL_WORKLOADS if args.workload == "mlp_down" else inputs.WORKLOADS)[args.workload]
     B = args.B if args.B is not None else d[0]
+    if args.workload == "mlp_down":
+        args.surface = args.op
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
@@ -321,6 +334,13 @@ def bench_partial(args):
                       device=dev)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
+    if args.copy_calibration_mib > 0:
+        src = torch.ones(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def call():
         sb.sb_partial_complete(part, args.op, out, ws=wsp, stream=stream)
@@ -344,7 +364,8 @@ def bench_partial(args):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "N": N, "K": Ks, "op": args.op},
         "roofline": dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
-                         unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                         unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                         traffic=recorded_traffic(args.workload, args.op, B),
                          kernel="whole call (chunked partial GEMM and the lane reduction)",
                          algorithmic_bytes=nbytes),
         "cpu_baseline": None, "report": {},
