@@ -363,6 +363,78 @@ __device__ void finish_tile(const HeadArgs &a, int lane, int group, int m0, int 
 // is left unconstrained (it fits 128 registers: 4 waves per SIMD); two row
 // blocks are held to 3 waves per SIMD (168 registers) and four to 2 (256),
 // both without spills.
+// Epilogue of one (row, 128-column tile) for the thread that holds the tile's
+// 8 columns from `colrel` (lane-relative; `gcol` global) of row b: the logits
+// or shard store, the (max, lowest index) key merged into the row's key of its
+// lane, and the written-through (tile max, sum-exp) pair.  The 16 threads of
+// a row are 16 consecutive lanes of one wave.
+template <int EPI>
+__device__ __forceinline__ void emit_tile_row(const HeadArgs &a, const float (&y)[8], int b,
+                                              bool rowok, int lane, int tile, int colrel,
+                                              int nvalid, int gcol, int cg)
+{
+    if (EPI == kEpiShard || EPI == kEpiPairLseOut) {
+        float *dst;
+        if (EPI == kEpiShard)
+            dst = a.lanes.shard[lane] + (int64_t)b * a.lanes.shard_ld[lane] + colrel;
+        else
+            dst = a.out + (int64_t)b * a.ldo + gcol;
+        if (rowok) {
+            if (nvalid == 8 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                *reinterpret_cast<f32x4 *>(dst) = f32x4{y[0], y[1], y[2], y[3]};
+                *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{y[4], y[5], y[6], y[7]};
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (j < nvalid)
+                        dst[j] = y[j];
+            }
+        }
+    }
+    if (EPI != kEpiShard) {
+        // (max, lowest index) over the thread's columns, ascending.
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+        if (nvalid > 0) {
+            bv = y[0];
+            bi = gcol;
+        }
+#pragma unroll
+        for (int j = 1; j < 8; ++j)
+            if (j < nvalid && y[j] > bv) {
+                bv = y[j];
+                bi = gcol + j;
+            }
+        // across the 16 threads of this row (one 16-lane row of the wave)
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 16);
+            const int oi = __shfl_xor(bi, o, 16);
+            if (better(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        float se = 0.f;
+        if (EPI != kEpiPair) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < nvalid)
+                    se += __expf(y[j] - bv);
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1)
+                se += __shfl_xor(se, o, 16);
+        }
+        if (cg == 0 && rowok) {
+            __hip_atomic_fetch_max(a.keys + (int64_t)b * a.lanes.k + lane, pack_key(bv, bi),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (EPI != kEpiPair)
+                store_through(&a.mse[(int64_t)b * a.T + tile], __float_as_uint(bv),
+                              __float_as_uint(se));
+        }
+    }
+}
+
 template <int MB>
 struct Occupancy {
     static constexpr int kBlocksPerCU = MB == 1 ? 1 : (MB == 2 ? 3 : 2);
@@ -484,69 +556,228 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
         const int b = m0 + kRowBlock * mb + erow;
         const bool rowok = b < a.B;
 
-        if (EPI == kEpiShard || EPI == kEpiPairLseOut) {
-            float *dst;
-            if (EPI == kEpiShard)
-                dst = a.lanes.shard[lane] + (int64_t)b * a.lanes.shard_ld[lane] + colrel;
-            else
-                dst = a.out + (int64_t)b * a.ldo + gcol0 + 8 * cg;
-            if (rowok) {
-                if (nvalid == 8 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                    *reinterpret_cast<f32x4 *>(dst) = f32x4{y[0], y[1], y[2], y[3]};
-                    *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{y[4], y[5], y[6], y[7]};
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        if (j < nvalid)
-                            dst[j] = y[j];
-                }
-            }
-        }
-        if (EPI != kEpiShard) {
-            // (max, lowest index) over the thread's columns, ascending.
-            float bv = -INFINITY;
-            int bi = INT_MAX;
-            if (nvalid > 0) {
-                bv = y[0];
-                bi = gcol0 + 8 * cg;
-            }
-#pragma unroll
-            for (int j = 1; j < 8; ++j)
-                if (j < nvalid && y[j] > bv) {
-                    bv = y[j];
-                    bi = gcol0 + 8 * cg + j;
-                }
-            // across the 16 threads of this row (one 16-lane row of the wave)
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 16);
-                const int oi = __shfl_xor(bi, o, 16);
-                if (better(ov, oi, bv, bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            float se = 0.f;
-            if (EPI != kEpiPair) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (j < nvalid)
-                        se += __expf(y[j] - bv);
-#pragma unroll
-                for (int o = 8; o >= 1; o >>= 1)
-                    se += __shfl_xor(se, o, 16);
-            }
-            if (cg == 0 && rowok) {
-                __hip_atomic_fetch_max(a.keys + (int64_t)b * a.lanes.k + lane, pack_key(bv, bi),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (EPI != kEpiPair)
-                    store_through(&a.mse[(int64_t)b * a.T + tile], __float_as_uint(bv),
-                                  __float_as_uint(se));
-            }
-        }
+        emit_tile_row<EPI>(a, y, b, rowok, lane, tile, colrel, nvalid, gcol0 + 8 * cg, cg);
     }
     if (EPI != kEpiShard)
         finish_tile<MB, EPI>(a, lane, group, m0, rows_here);
+}
+
+// ---------------------------------------------------------------------------
+// Head GEMM for more than 64 rows (several row groups of four 16-row blocks):
+// two weight tiles per workgroup that share the hidden-row fragments.
+//
+// With 64 rows per group the hidden-row fragments of a step are half the size
+// of its weight slab, and every workgroup re-reads them through the L2.  Here
+// the 4 waves of a workgroup cover two
+// adjacent 128-column tiles, with the K steps split two ways: wave w computes
+// tile w & 1 over the steps h, h + 2, h + 4, ... of its half h = w >> 1.  The
+// two waves of a half load two of the four row blocks each and exchange them
+// through LDS, so the hidden rows are read once per tile pair.  Each logit is
+// (sum over half 0) + (sum over half 1), each half summed in ascending K
+// order, whatever the tile's position; the three surfaces stay bit-identical.
+// ---------------------------------------------------------------------------
+constexpr int kXRows = kMaxMB * 64;  // u32x4 per (parity, K half): 4 row blocks x 64 lanes
+
+template <int POL>
+__device__ __forceinline__ void load_pair_step(Frags<kMaxMB> &f, const uint16_t *wbase,
+                                               int64_t wbytes, const uint16_t *xbase,
+                                               int64_t xbytes, int k0, int64_t ldw,
+                                               const uint32_t (&wvo)[8], const uint32_t (&xvo)[2])
+{
+    const int64_t wshift = (int64_t)k0 * ldw;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + wshift, wbytes - wshift * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + k0, xbytes - (int64_t)k0 * 2);
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        f.w[r] = load16w<POL>(rw, wvo[r]);
+    // this wave's half of the hidden-row fragments, exchanged before use
+    f.x[0] = load16(rx, xvo[0]);
+    f.x[1] = load16(rx, xvo[1]);
+}
+
+template <int EPI, int POL>
+__global__ __launch_bounds__(kThreads, Occupancy<kMaxMB>::kBlocksPerCU) void head_gemm_pair_kernel(
+    const HeadArgs a)
+{
+    constexpr int MB = kMaxMB;
+    __shared__ float red[kWaves][kRowBlock][kTileN + 4];
+    __shared__ u32x4 xs[2][2][kXRows];  // [step parity][K half][row block][lane]
+
+    // 1-D grid in blocks of 8 tile pairs x all row groups, as the one-tile kernel
+    const int ntiles = a.lanes.tile0[a.lanes.k];
+    const int npairs = (ntiles + 1) / 2;
+    const int groups = (a.B + kRowBlock * MB - 1) / (kRowBlock * MB);
+    const int q = blockIdx.x >> 3;
+    const int pair = (q / groups) * 8 + (blockIdx.x & 7);
+    const int group = q - (q / groups) * groups;
+    if (pair >= npairs)
+        return;
+    const bool second = 2 * pair + 1 < ntiles;  // the pair's second tile exists
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int L = threadIdx.x & 63;
+    const int n = L & 15;
+    const int g = L >> 4;
+    const int t = wave & 1, h = wave >> 1;
+    const int H = a.H;
+    const int m0 = group * (kRowBlock * MB);
+    const int rows_here = min(a.B - m0, kRowBlock * MB);
+
+    // geometry of both tiles (the epilogue handles both); a missing second
+    // tile takes the first one's lane and reads no weight
+    int lane2[2], c02[2], vi2[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tl = (u == 1 && second) ? 2 * pair + 1 : 2 * pair;
+        lane2[u] = find_lane(a.lanes, tl);
+        vi2[u] = a.lanes.off[lane2[u] + 1] - a.lanes.off[lane2[u]];
+        c02[u] = (tl - a.lanes.tile0[lane2[u]]) * kTileN - a.lanes.shift[lane2[u]];
+    }
+    const int lane = t ? lane2[1] : lane2[0];
+    const int c0 = t ? c02[1] : c02[0];
+    const int Vi = t ? vi2[1] : vi2[0];
+    const bool reads_w = t == 0 || second;
+    const int cb = max(c0, 0);
+    const uint16_t *wbase = a.lanes.w[lane] + cb;
+    const int64_t wcols = ((int64_t)(Vi - cb) + 7) & ~(int64_t)7;
+    const int64_t wbytes = reads_w && H > 0 ? (((int64_t)(H - 1) * a.ldw) + wcols) * 2 : 0;
+    const uint16_t *xbase = a.x + (int64_t)m0 * a.ldx;
+    const int64_t xbytes = H > 0 ? (((int64_t)(rows_here - 1) * a.ldx) + ((H + 7) & ~7)) * 2 : 0;
+
+    uint32_t wvo[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        wvo[r] = (uint32_t)(((int64_t)(8 * g + r) * a.ldw + max(c0 + 8 * n - cb, 0)) * 2);
+    uint32_t xvo[2];  // row blocks 2t and 2t + 1
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        xvo[j] = (uint32_t)(((int64_t)(kRowBlock * (2 * t + j) + n) * a.ldx + 8 * g) * 2);
+
+    f32x4 acc[MB][8];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            acc[mb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // This wave's steps are h, h + 2, ...: nw of them.  Every wave runs nmax
+    // exchange steps (one barrier each); steps past H only see masked zeros.
+    const int nsteps = (H + kStepK - 1) / kStepK;
+    const int nmax = (nsteps + 1) / 2;
+    const int nw = nsteps > h ? (nsteps - h + 1) / 2 : 0;
+    constexpr int kStride = 2 * kStepK;
+    Frags<MB> fa, fb;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        fa.w[r] = u32x4{0u, 0u, 0u, 0u};
+        fb.w[r] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+        fa.x[j] = u32x4{0u, 0u, 0u, 0u};
+        fb.x[j] = u32x4{0u, 0u, 0u, 0u};
+    }
+    auto step = [&](Frags<MB> &f, int i, int k0) {
+        // publish this wave's half, then take all four row blocks; parity i
+        // alternates, so a slot is rewritten only after the next barrier
+        u32x4 *slot = &xs[i & 1][h][0];
+        slot[(2 * t) * 64 + L] = f.x[0];
+        slot[(2 * t + 1) * 64 + L] = f.x[1];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+            f.x[j] = slot[j * 64 + L];
+        compute_step<MB>(f, acc, k0, H, g);
+    };
+    int k0 = h * kStepK;
+    if (nw > 0)
+        load_pair_step<POL>(fa, wbase, wbytes, xbase, xbytes, k0, a.ldw, wvo, xvo);
+    int i = 0;
+    for (; i + 2 <= nmax; i += 2) {
+        if (i + 1 < nw)
+            load_pair_step<POL>(fb, wbase, wbytes, xbase, xbytes, k0 + kStride, a.ldw, wvo, xvo);
+        step(fa, i, k0);
+        if (i + 2 < nw)
+            load_pair_step<POL>(fa, wbase, wbytes, xbase, xbytes, k0 + 2 * kStride, a.ldw, wvo, xvo);
+        step(fb, i + 1, k0 + kStride);
+        k0 += 2 * kStride;
+    }
+    if (nmax & 1)
+        step(fa, i, k0);
+
+    // ---------------- epilogue, one 16-row block at a time ----------------
+    const int erow = threadIdx.x >> 4;  // 0..15: row inside the block
+    const int cg = threadIdx.x & 15;    // 8-column group inside the tile
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        if (m0 + kRowBlock * mb >= a.B)
+            break;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            f32x4 lo = {acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+            f32x4 hi = {acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
+            *reinterpret_cast<f32x4 *>(&red[wave][4 * g + r][8 * n]) = lo;
+            *reinterpret_cast<f32x4 *>(&red[wave][4 * g + r][8 * n + 4]) = hi;
+        }
+        __syncthreads();
+        // tile u: half 0 in wave u, half 1 in wave u + 2
+        float y[2][8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const f32x4 p0l = *reinterpret_cast<const f32x4 *>(&red[u][erow][8 * cg]);
+            const f32x4 p0h = *reinterpret_cast<const f32x4 *>(&red[u][erow][8 * cg + 4]);
+            const f32x4 p1l = *reinterpret_cast<const f32x4 *>(&red[u + 2][erow][8 * cg]);
+            const f32x4 p1h = *reinterpret_cast<const f32x4 *>(&red[u + 2][erow][8 * cg + 4]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                y[u][j] = p0l[j] + p1l[j];
+                y[u][j + 4] = p0h[j] + p1h[j];
+            }
+        }
+        __syncthreads();  // LDS free for the next block
+
+        const int b = m0 + kRowBlock * mb + erow;
+        const bool rowok = b < a.B;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (u == 1 && !second)
+                break;
+            const int colrel = c02[u] + 8 * cg;
+            const int nvalid = colrel < 0 ? 0 : max(0, min(8, vi2[u] - colrel));
+            emit_tile_row<EPI>(a, y[u], b, rowok, lane2[u], 2 * pair + u, colrel, nvalid,
+                               a.lanes.off[lane2[u]] + colrel, cg);
+        }
+    }
+    if (EPI != kEpiShard) {
+        finish_tile<MB, EPI>(a, lane2[0], group, m0, rows_here);
+        if (second)
+            finish_tile<MB, EPI>(a, lane2[1], group, m0, rows_here);
+    }
+}
+
+template <int POL>
+hipError_t launch_pair(const HeadArgs &a, int epi, hipStream_t s)
+{
+    const int rpg = kRowBlock * kMaxMB;
+    const int npairs = (a.lanes.tile0[a.lanes.k] + 1) / 2;
+    dim3 grid(((npairs + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg));
+    switch (epi) {
+    case kEpiPair:
+        hipLaunchKernelGGL((head_gemm_pair_kernel<kEpiPair, POL>), grid, dim3(kThreads), 0, s, a);
+        break;
+    case kEpiPairLse:
+        hipLaunchKernelGGL((head_gemm_pair_kernel<kEpiPairLse, POL>), grid, dim3(kThreads), 0, s, a);
+        break;
+    case kEpiPairLseOut:
+        hipLaunchKernelGGL((head_gemm_pair_kernel<kEpiPairLseOut, POL>), grid, dim3(kThreads), 0, s, a);
+        break;
+    case kEpiShard:
+        hipLaunchKernelGGL((head_gemm_pair_kernel<kEpiShard, POL>), grid, dim3(kThreads), 0, s, a);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 // One workgroup per row: fold the per-tile results lane by lane.
@@ -1316,9 +1547,11 @@ hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s)
     case 2:
         return launch_mb<2, kPolicyStream>(a, epi, s);
     default:
+        // One row group streams each weight tile once; with several row
+        // groups two tiles per workgroup share the hidden rows.
         if (a.B <= kRowBlock * kMaxMB)
             return launch_mb<kMaxMB, kPolicyStream>(a, epi, s);
-        return launch_mb<kMaxMB, kPolicyShared>(a, epi, s);
+        return launch_pair<kPolicyShared>(a, epi, s);
     }
 }
 

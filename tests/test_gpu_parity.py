@@ -67,7 +67,7 @@ def test_small_heads(require_gpu, B, H, V, off, sep):
     _case(d, lanes_separate=sep)
 
 
-@pytest.mark.parametrize("B", [9, 260])
+@pytest.mark.parametrize("B", [9, 100, 260])
 def test_non_finite_padding_is_never_read(require_gpu, B):
     H, V = 100, 700
     off = [0, 200, 433, 700]
@@ -77,7 +77,7 @@ def test_non_finite_padding_is_never_read(require_gpu, B):
     assert np.array_equal(g["logits"], g2["logits"])
 
 
-@pytest.mark.parametrize("B", [16, 40, 300])
+@pytest.mark.parametrize("B", [16, 40, 100, 300])
 def test_lane_base_alignment(require_gpu, B):
     """Shards that start at 16-byte positions inside a 128-byte cache line
     (each lane's tile grid then starts up to 56 columns before its first
@@ -104,7 +104,7 @@ def test_batch_boundaries(require_gpu, B):
     _case(d, lanes_separate=(B % 2 == 1))
 
 
-@pytest.mark.parametrize("B,sep", [(16, False), (40, True), (300, False)])
+@pytest.mark.parametrize("B,sep", [(16, False), (40, True), (100, True), (300, False)])
 def test_maximum_lane_count(require_gpu, B, sep):
     """k = 64 lanes (the ABI's maximum), widths from 8 to 1000 columns."""
     widths = [(8, 16, 136, 264, 1000, 24, 128, 504)[i % 8] for i in range(64)]
