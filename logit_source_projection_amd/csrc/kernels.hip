@@ -316,21 +316,24 @@ __device__ void finish_tile(const HeadArgs &a, int lane, int group, int m0, int 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     // Thread j of a row merges tiles t0 + j, t0 + j + w, ... in ascending
-    // order (loads issued four at a time), then a fixed butterfly.
+    // order (loads issued kFoldBatch at a time: with 64 rows a thread folds
+    // about 150 tiles, and each batch costs one memory round trip), then a
+    // fixed butterfly.
     {
+        constexpr int kFoldBatch = 32;
         const int w = fold_width(rows_here);
         const int r = threadIdx.x / w, j = threadIdx.x % w;
         const int b = m0 + r;
         float m = -INFINITY, se = 0.f;
         if (r < rows_here) {
             const float2 *row = a.mse + (int64_t)b * a.T;
-            for (int t = t0 + j; t < t1; t += 4 * w) {
-                float2 q[4];
+            for (int t = t0 + j; t < t1; t += kFoldBatch * w) {
+                float2 q[kFoldBatch];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < kFoldBatch; ++u)
                     q[u] = t + u * w < t1 ? row[t + u * w] : make_float2(-INFINITY, 0.f);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+                for (int u = 0; u < kFoldBatch; ++u)
                     lse_merge(m, se, q[u].x, q[u].y);
             }
         }
