@@ -115,6 +115,19 @@ def test_maximum_lane_count(require_gpu, B, sep):
     _case(d, lanes_separate=sep)
 
 
+@pytest.mark.parametrize("B,H,V,off", [
+    (3, 64, 1, [0, 1]),              # a single vocabulary column
+    (5, 32, 8, list(range(9))),      # eight lanes of one column each
+    (40, 1, 300, [0, 100, 300]),     # H = 1: one product per logit
+    (70, 1, 300, [0, 100, 300]),     # ... with two tiles per workgroup
+])
+def test_degenerate_heads(require_gpu, B, H, V, off):
+    """Smallest vocabularies, one-column lanes and a one-element hidden size
+    (the hidden rows padded to the 8-element stride with non-finite bits)."""
+    d = inputs.make_random(B, H, V, off, seed=B + V)
+    _case(d, lanes_separate=True, pad_x=(8 - H % 8) % 8)
+
+
 def test_maximum_batch(require_gpu):
     """B = 65535 (the ABI's maximum): 256 row blocks of the large-batch kernel."""
     d = inputs.make_random(65535, 40, 520, [0, 256, 520], seed=3000)

@@ -72,6 +72,8 @@ CASES = [
     (64, (777, 31, 1500), 520),
     (65, (512,), 64),
     (300, (700, 700), 200),
+    (3, (1, 9), 1),       # one output column, a one-row shard
+    (2, (31,), 8),
 ]
 
 
