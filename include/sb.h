@@ -45,10 +45,17 @@
  *    owned by the call until its work completes on the stream; calls that
  *    share one workspace must be ordered on one stream.
  *  - A workspace must be ZERO-FILLED before its first use (allocate it once,
- *    zeroed, and reuse it).  For B < 256 the token and log-prob calls keep
- *    completion counters and per-lane result keys at its start; every call
- *    that completes leaves them zero, so a workspace stays valid for later
- *    calls of any shape.
+ *    zeroed, and reuse it).  Every workspace starts with the same fixed
+ *    region (140,032 bytes) of completion counters, per-lane result keys and
+ *    per-tile slice counters.  Calls read it only where it is zero on entry
+ *    and leave it zero when they complete, and no call writes anything else
+ *    there, so one workspace (sized for the largest call) stays valid for
+ *    later calls of any shape, surface or entry point, partial completion
+ *    included.
+ *  - A head of fewer than 128 vocabulary tiles of 128 columns (B <= 64) splits
+ *    each tile's hidden sum into up to 8 slices that run as separate
+ *    workgroups; the slice partials are added in slice order.  The split
+ *    depends on (B, H, V) only, so the guarantees above still hold.
  *
  * Errors
  *  - Validation is synchronous: on any error status nothing is enqueued and
@@ -216,9 +223,11 @@ typedef struct sb_partial_desc {
 } sb_partial_desc;
 
 /*
- * Bytes of device workspace sb_partial_complete needs on `desc` (the fp32
- * chunk partials; no zero-fill needed).  Returns 0 and sets *status on an
- * invalid descriptor (statuses as for the head; SB_ERR_LANES for bad lane_k).
+ * Bytes of device workspace sb_partial_complete needs on `desc`: the head
+ * calls' fixed zeroed region, which this call leaves untouched, then the fp32
+ * chunk partials (no zero-fill needed for this call alone).  0 for B == 0.
+ * Returns 0 and sets *status on an invalid descriptor (statuses as for the
+ * head; SB_ERR_LANES for bad lane_k).
  */
 size_t sb_partial_workspace_bytes(const sb_partial_desc *desc, sb_status *status);
 

@@ -63,6 +63,14 @@ struct HeadArgs {
     int32_t *ids;        // [B]
     float *lse;          // [B] or null
     float *sel_lp;       // [B] or null
+    // K slices (head_gemm_kernel, one row group): the hidden steps of every
+    // tile are split into kslices contiguous runs of slice_steps steps, one
+    // workgroup each; each writes its partial tile to kpart and the last to
+    // finish a tile adds the kslices partials in slice order.
+    int32_t kslices;             // 1 = no split
+    int32_t slice_steps;         // kStepK-row steps per slice, a multiple of kWaves
+    float *kpart;                // [T][kslices][rows per group][kTileN] fp32 partial tiles
+    uint32_t *kctr;              // [T] per-tile slice counters: zero on entry, left zero
 };
 
 // Tiles of a lane of vi columns whose grid starts `shift` columns early.
@@ -75,6 +83,46 @@ inline int lane_tiles(int vi, int shift) { return (vi + shift + kTileN - 1) / kT
 inline int rows_per_group(int B)
 {
     return B <= kRowBlock ? kRowBlock : (B <= 2 * kRowBlock ? 2 * kRowBlock : kMaxMB * kRowBlock);
+}
+
+// K slices for a head of few tiles.  One workgroup streams one 128-column
+// tile at a few tens of GB/s, so a head of fewer than kSplitBelowTiles tiles
+// leaves most of the 256 CUs idle.  Such a head splits every tile's hidden
+// steps into slices of at least kMinSliceSteps steps, up to kMaxSlices of
+// them, so that about kSplitTarget workgroups (one per CU) run.  Larger heads
+// are not split: one workgroup per tile streamed fastest from 128 tiles up in
+// timings of 1 to 8 slices (a split adds a partial-tile write and a fold per
+// slice).  The split depends on (B, H, V) only -- not on the lane split or
+// the shard placement -- so every surface and every lane split of a head sums
+// each logit in the same order.
+constexpr int kSplitBelowTiles = 128;
+constexpr int kSplitTarget = 256;
+constexpr int kMinSliceSteps = 16;
+constexpr int kMaxSlices = 8;
+constexpr int kMaxSplitTiles = 2048;  // tile capacity of the slice counters
+static_assert(kSplitBelowTiles + 2 * kMaxLanes <= kMaxSplitTiles,
+              "a split head's tiles, shifted lanes included, fit the counters");
+inline int k_slices(int B, int H, int V)
+{
+    if (B <= 0 || B > kRowBlock * kMaxMB || H <= 0 || V <= 0)
+        return 1;
+    const int tiles = (V + kTileN - 1) / kTileN;
+    const int nsteps = (H + kStepK - 1) / kStepK;
+    if (tiles >= kSplitBelowTiles)
+        return 1;
+    int s = (kSplitTarget + tiles - 1) / tiles;
+    s = s < kMaxSlices ? s : kMaxSlices;
+    s = s < nsteps / kMinSliceSteps ? s : nsteps / kMinSliceSteps;
+    if (s <= 1)
+        return 1;
+    // whole multiples of kWaves steps per slice, and no empty slice
+    const int per = ((nsteps + s - 1) / s + kWaves - 1) / kWaves * kWaves;
+    return (nsteps + per - 1) / per;
+}
+inline int slice_steps(int H, int slices)
+{
+    const int nsteps = (H + kStepK - 1) / kStepK;
+    return slices <= 1 ? nsteps : ((nsteps + slices - 1) / slices + kWaves - 1) / kWaves * kWaves;
 }
 
 // Launch the head GEMM with the given epilogue.  For every epilogue except

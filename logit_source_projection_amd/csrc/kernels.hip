@@ -448,15 +448,18 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
 {
     __shared__ float red[kWaves][kRowBlock][kTileN + 4];
 
-    // 1-D grid in blocks of 8 tiles x all row groups: the row groups of one
-    // weight tile get workgroup ids 8 apart.  Workgroups are handed to the 8
-    // XCDs round-robin, so they share one XCD's L2 and all but the first
-    // read the tile from it (a placement hint only; results do not depend on
-    // where a workgroup runs).  Ids past the last tile exit at once.
+    // 1-D grid in blocks of 8 tiles x all row groups (or all K slices): the
+    // row groups of one weight tile get workgroup ids 8 apart.  Workgroups
+    // are handed to the 8 XCDs round-robin, so they share one XCD's L2 and
+    // all but the first read the tile from it (a placement hint only;
+    // results do not depend on where a workgroup runs).  Ids past the last
+    // tile exit at once.  A head split into K slices has one row group.
     const int groups = (a.B + kRowBlock * MB - 1) / (kRowBlock * MB);
+    const int per_tile = groups * a.kslices;
     const int q = blockIdx.x >> 3;
-    const int tile = (q / groups) * 8 + (blockIdx.x & 7);
-    const int group = q - (q / groups) * groups;
+    const int tile = (q / per_tile) * 8 + (blockIdx.x & 7);
+    const int group = (q - (q / per_tile) * per_tile) % groups;
+    const int slice = (q - (q / per_tile) * per_tile) / groups;
     if (tile >= a.lanes.tile0[a.lanes.k])
         return;
     const int lane = find_lane(a.lanes, tile);
@@ -499,15 +502,19 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
         for (int c = 0; c < 8; ++c)
             acc[mb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // This wave's steps are wave, wave + 4, ...: nw of them, taken in pairs
-    // (one step loading while the other computes) with a single exit at the
-    // end of a pair, so that the accumulators stay in place.
+    // The slice's steps are s_begin .. s_end - 1 (all steps without a split).
+    // This wave's steps are s_begin + wave, s_begin + wave + 4, ...: nw of
+    // them, taken in pairs (one step loading while the other computes) with
+    // a single exit at the end of a pair, so that the accumulators stay in
+    // place.
     const int nsteps = (H + kStepK - 1) / kStepK;
-    const int nw = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;
+    const int s_begin = slice * a.slice_steps;
+    const int s_len = min(s_begin + a.slice_steps, nsteps) - s_begin;
+    const int nw = s_len > wave ? (s_len - wave + kWaves - 1) / kWaves : 0;
     Frags<MB> fa, fb;
+    int k0 = (s_begin + wave) * kStepK;
     if (nw > 0)
-        load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, wave * kStepK, a.ldw, wvo, xvo);
-    int k0 = wave * kStepK;
+        load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, k0, a.ldw, wvo, xvo);
     for (int i = 0; i + 2 <= nw; i += 2) {
         load_step<MB, POL>(fb, wbase, wbytes, xbase, xbytes, k0 + kWaves * kStepK, a.ldw, wvo,
                            xvo);
@@ -559,7 +566,50 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
         const int b = m0 + kRowBlock * mb + erow;
         const bool rowok = b < a.B;
 
+        if (a.kslices > 1) {
+            // this slice's partial tile, written through for the last slice
+            float *p = a.kpart + ((size_t)tile * a.kslices + slice) * (kRowBlock * MB * kTileN) +
+                       (kRowBlock * mb + erow) * kTileN + 8 * cg;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                store_through(p + 2 * j, __float_as_uint(y[2 * j]), __float_as_uint(y[2 * j + 1]));
+            continue;
+        }
         emit_tile_row<EPI>(a, y, b, rowok, lane, tile, colrel, nvalid, gcol0 + 8 * cg, cg);
+    }
+    if (a.kslices > 1) {
+        // The workgroup that finishes a tile's last slice adds the partial
+        // tiles in slice order and runs the epilogue; the others are done.
+        __shared__ int s_fold;
+        wait_all_memory();
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t old = atomicAdd(a.kctr + tile, 1u);
+            s_fold = old == (uint32_t)(a.kslices - 1);
+        }
+        __syncthreads();
+        if (!s_fold)
+            return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (threadIdx.x == 0)
+            __hip_atomic_store(a.kctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if (m0 + kRowBlock * mb >= a.B)
+                break;
+            const float *p = a.kpart + (size_t)tile * a.kslices * (kRowBlock * MB * kTileN) +
+                             (kRowBlock * mb + erow) * kTileN + 8 * cg;
+            f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
+            f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 4);
+            for (int sl = 1; sl < a.kslices; ++sl) {
+                p += kRowBlock * MB * kTileN;
+                lo += *reinterpret_cast<const f32x4 *>(p);
+                hi += *reinterpret_cast<const f32x4 *>(p + 4);
+            }
+            const float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const int b = m0 + kRowBlock * mb + erow;
+            emit_tile_row<EPI>(a, y, b, b < a.B, lane, tile, colrel, nvalid, gcol0 + 8 * cg, cg);
+        }
     }
     if (EPI != kEpiShard)
         finish_tile<MB, EPI>(a, lane, group, m0, rows_here);
@@ -1346,7 +1396,7 @@ hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
 {
     const int rpg = kRowBlock * MB;
     const int ntiles = a.lanes.tile0[a.lanes.k];
-    dim3 grid(((ntiles + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg));
+    dim3 grid(((ntiles + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg) * a.kslices);
     switch (epi) {
     case kEpiPair:
         hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPair, POL>), grid, dim3(kThreads), 0, s, a);

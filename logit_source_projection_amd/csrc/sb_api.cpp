@@ -18,6 +18,26 @@ constexpr size_t kRegionAlign = 256;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Every workspace starts with the same fixed region that must be zero on
+// entry and that every call leaves zero: completion counters (row groups x
+// lanes), per-lane keys (rows x lanes, for B < 256) and per-tile slice
+// counters.  Its size does not depend on the call, so no call -- of any
+// shape, surface or entry point -- writes non-zero data where a later call
+// expects zeros.
+constexpr int kSmallGroups =
+    (sbk::kLargeBatch - 1 + sbk::kRowBlock * sbk::kMaxMB - 1) / (sbk::kRowBlock * sbk::kMaxMB);
+constexpr size_t kZeroSync = 0;
+constexpr size_t kZeroKeys =
+    (kZeroSync + kSmallGroups * (SB_MAX_LANES + 1) * sizeof(uint32_t) + kRegionAlign - 1) /
+    kRegionAlign * kRegionAlign;
+constexpr size_t kZeroSlices =
+    (kZeroKeys + (size_t)(sbk::kLargeBatch - 1) * SB_MAX_LANES * sizeof(uint64_t) +
+     kRegionAlign - 1) / kRegionAlign * kRegionAlign;
+constexpr size_t kZeroBytes =
+    (kZeroSlices + sbk::kMaxSplitTiles * sizeof(uint32_t) + kRegionAlign - 1) / kRegionAlign *
+    kRegionAlign;
+static_assert(kZeroBytes == 140032, "the size include/sb.h states for the zeroed region");
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Validation of the head descriptor (shapes, lanes, alignment, limits).
@@ -73,7 +93,8 @@ struct Layout {
     int T = 0;            // tile capacity: row stride of the (row, tile) regions
     int nchunks = 0;      // full-logit argmax chunks per row
     int groups = 0;       // row groups (grid y) of the head GEMM
-    size_t sync = 0, keys = 0, pair = 0, mse = 0, lane_mse = 0;
+    int kslices = 1;      // K slices of the head GEMM (one row group only)
+    size_t sync = 0, keys = 0, kctr = 0, kpart = 0, pair = 0, mse = 0, lane_mse = 0;
     size_t shard[SB_MAX_LANES] = {}, partial = 0;
     size_t total = 0;
 };
@@ -94,6 +115,17 @@ Layout layout(const sb_head_desc *d, int surface)
     L.groups = (d->B + rpg - 1) / rpg;
     const bool large = d->B >= sbk::kLargeBatch;
     const bool lse = surface == SB_SURF_LOGPROBS || surface == SB_SURF_LOGPROBS_FULL;
+    L.sync = kZeroSync;
+    L.keys = kZeroKeys;
+    L.kctr = kZeroSlices;
+    at = kZeroBytes;
+    L.kslices = sbk::k_slices(d->B, d->H, d->V);
+    if (L.kslices > 1) {
+        // partial tiles of the K slices, [T][kslices][rows per group][kTileN]
+        L.kpart = at;
+        at = align_up(at + (size_t)L.T * L.kslices * rpg * sbk::kTileN * sizeof(float),
+                      kRegionAlign);
+    }
     switch (surface) {
     case SB_SURF_TOKENS:
     case SB_SURF_LOGPROBS:
@@ -108,12 +140,7 @@ Layout layout(const sb_head_desc *d, int surface)
             }
             break;
         }
-        // completion counters and lane keys first: the regions that must
-        // start zeroed (every call leaves them zeroed)
-        L.sync = at;
-        at = align_up(at + (size_t)L.groups * (d->k + 1) * sizeof(uint32_t), kRegionAlign);
-        L.keys = at;
-        at = align_up(at + B * d->k * sizeof(uint64_t), kRegionAlign);
+        // completion counters and lane keys: in the zeroed region
         if (lse) {
             L.mse = at;
             at = align_up(at + B * L.T * sizeof(float2), kRegionAlign);
@@ -135,6 +162,12 @@ Layout layout(const sb_head_desc *d, int surface)
     }
     L.total = at;
     return L;
+}
+
+template <typename T>
+T *region(void *ws, size_t off)
+{
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
 void fill_lanes(const sb_head_desc *d, sbk::LaneTable &t)
@@ -178,6 +211,19 @@ void fill_args(const sb_head_desc *d, const Layout &L, sbk::HeadArgs &a)
     a.ids = nullptr;
     a.lse = nullptr;
     a.sel_lp = nullptr;
+    a.kslices = L.kslices;
+    a.slice_steps = sbk::slice_steps(d->H, L.kslices);
+    a.kpart = nullptr;
+    a.kctr = nullptr;
+}
+
+// The K-slice regions of a split head (a no-op without a split).
+void set_slices(const Layout &L, void *ws, sbk::HeadArgs &a)
+{
+    if (L.kslices > 1) {
+        a.kpart = region<float>(ws, L.kpart);
+        a.kctr = region<uint32_t>(ws, L.kctr);
+    }
 }
 
 sb_status check_ws(const Layout &L, void *ws, size_t ws_bytes)
@@ -193,11 +239,6 @@ sb_status check_ws(const Layout &L, void *ws, size_t ws_bytes)
     return SB_OK;
 }
 
-template <typename T>
-T *region(void *ws, size_t off)
-{
-    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
-}
 
 // ---------------------------------------------------------------------------
 // Partial completion
@@ -249,11 +290,15 @@ int partial_chunks(const sb_partial_desc *d)
     return n;
 }
 
+// The chunk partials sit after the head calls' zeroed region, so that one
+// workspace can serve both kinds of call.
 size_t partial_bytes(const sb_partial_desc *d)
 {
-    return align_up((size_t)partial_chunks(d) * (size_t)d->B * (size_t)shard_ld(d->N) *
-                        sizeof(float),
-                    kRegionAlign);
+    if (d->B == 0)
+        return 0;  // nothing is read or written
+    return kZeroBytes + align_up((size_t)partial_chunks(d) * (size_t)d->B *
+                                     (size_t)shard_ld(d->N) * sizeof(float),
+                                 kRegionAlign);
 }
 
 }  // namespace
@@ -299,6 +344,7 @@ sb_status sb_project_tokens(const sb_head_desc *desc, int32_t *ids, void *ws, si
     }
     a.sync = region<uint32_t>(ws, L.sync);
     a.keys = region<unsigned long long>(ws, L.keys);
+    set_slices(L, ws, a);
     if (sbk::launch_head_gemm(a, sbk::kEpiPair, s) != hipSuccess)
         return SB_ERR_HIP;
     return SB_OK;
@@ -334,6 +380,7 @@ sb_status sb_project_logprobs(const sb_head_desc *desc, int32_t *ids, float *lse
         a.sync = region<uint32_t>(ws, L.sync);
         a.keys = region<unsigned long long>(ws, L.keys);
         a.lane_mse = region<float2>(ws, L.lane_mse);
+        set_slices(L, ws, a);
     }
     a.ids = ids;
     a.lse = lse;
@@ -378,6 +425,7 @@ sb_status sb_full_logits(const sb_head_desc *desc, float *logits, int64_t ldl, i
         a.lanes.shard[i] = region<float>(ws, L.shard[i]);
         a.lanes.shard_ld[i] = shard_ld(lane_width(desc, i));
     }
+    set_slices(L, ws, a);
     const hipError_t e = a.B >= sbk::kLargeBatch ? sbk::launch_head_gemm_large(a, sbk::kEpiShard, s)
                                                   : sbk::launch_head_gemm(a, sbk::kEpiShard, s);
     if (e != hipSuccess)
@@ -438,7 +486,7 @@ sb_status sb_partial_complete(const sb_partial_desc *desc, int op, float *out, i
     a.B = desc->B;
     a.N = desc->N;
     a.T = (desc->N + sbk::kTileN - 1) / sbk::kTileN;
-    a.part = static_cast<float *>(ws);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + kZeroBytes);
     a.ldp = shard_ld(desc->N);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (sbk::launch_partial_gemm(a, s) != hipSuccess ||

@@ -70,22 +70,55 @@ def tokens_status(head, ids=FAKE, ws=FAKE, ws_bytes=1 << 30):
     return sb.lib().sb_project_tokens(head.ref(), ids, ws, ws_bytes, None)
 
 
+def up256(n):
+    return (n + 255) // 256 * 256
+
+
+# Every workspace starts with one fixed zeroed region, whatever the call:
+# completion counters for up to 4 row groups x 65, per-lane keys for up to
+# 255 rows x 64 lanes (8 B each), then 2048 per-tile slice counters.
+ZERO = up256(up256(up256(4 * 65 * 4) + 255 * 64 * 8) + 2048 * 4)
+
+
 def test_workspace_bytes_for_the_workloads():
+    assert ZERO == 140032
     h = fake_head(B=16, H=5120, V=151936, off=(0, 37984, 75968, 113952, 151936))
     # tile capacity per lane: ceil((37984 + 56) / 128), room for a lane grid
     # shifted by up to 56 columns onto a cache-line boundary
     T = 4 * 298
-    # completion counters (256 B), per-lane keys (16 rows x 4 lanes x 8 B)
-    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == 256 + 512
+    # the dense head has enough tiles (1187) for one workgroup each: no slices
+    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == ZERO
     # + per-tile (max, sum-exp) pairs and per-lane pairs
     lp = sb.sb_workspace_bytes(h, sb.SB_SURF_LOGPROBS)
-    assert lp == 256 + 512 + 16 * T * 8 + 512
+    assert lp == ZERO + 16 * T * 8 + 512
     # large batches: per-tile pairs for the combine kernel only
     hl = fake_head(B=300, H=5120, V=151936, off=(0, 37984, 75968, 113952, 151936))
-    assert sb.sb_workspace_bytes(hl, sb.SB_SURF_TOKENS) == (300 * T * 8 + 255) // 256 * 256
+    assert sb.sb_workspace_bytes(hl, sb.SB_SURF_TOKENS) == ZERO + up256(300 * T * 8)
     full = sb.sb_workspace_bytes(h, sb.SB_SURF_FULL_LOGITS)
-    assert full >= 16 * 151936 * 4
+    assert full >= ZERO + 16 * 151936 * 4
     assert sb.sb_workspace_bytes(fake_head(B=0), sb.SB_SURF_TOKENS) == 0
+
+
+def test_workspace_bytes_of_a_split_head():
+    # A head of 64 tiles (V = 8192) splits its 160 hidden steps into 4 slices
+    # of 40, and each slice writes a 16 x 128 fp32 partial tile per tile of
+    # the capacity (65 tiles, with room for a lane grid shifted by 56 columns).
+    h = fake_head(B=16, H=5120, V=8192, off=(0, 8192))
+    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == ZERO + 65 * 4 * 16 * 128 * 4
+    # the split depends on (B, H, V), not on the lane split
+    h4 = fake_head(B=16, H=5120, V=8192, off=(0, 2048, 4096, 6144, 8192))
+    assert sb.sb_workspace_bytes(h4, sb.SB_SURF_TOKENS) == ZERO + 4 * 17 * 4 * 16 * 128 * 4
+    # 127 tiles: 3 slices (of 56, 56 and 48 steps); 64 rows: 64-row partial tiles
+    h = fake_head(B=64, H=5120, V=16256, off=(0, 16256))
+    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == ZERO + 128 * 3 * 64 * 128 * 4
+    # one GPU's lane of the dense head (297 tiles) and of the MoE head: no split
+    assert sb.sb_workspace_bytes(fake_head(B=16, H=5120, V=37984, off=(0, 37984)),
+                                 sb.SB_SURF_TOKENS) == ZERO
+    assert sb.sb_workspace_bytes(fake_head(B=64, H=4096, V=75968, off=(0, 75968)),
+                                 sb.SB_SURF_TOKENS) == ZERO
+    # fewer than 32 hidden steps (H <= 992): never split
+    assert sb.sb_workspace_bytes(fake_head(B=16, H=992, V=1024, off=(0, 1024)),
+                                 sb.SB_SURF_TOKENS) == ZERO
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -180,11 +213,12 @@ def partial_status(p, op=sb.SB_RED_SUM, out=FAKE, ldo=None, ws=FAKE, ws_bytes=1 
 
 def test_partial_workspace_bytes():
     # two lanes of 8704 rows -> 9 + 9 chunks of 1024 rows, fp32 [B][N] each
+    # (after the head calls' zeroed region, so that one workspace serves both)
     p = fake_partial()
-    assert sb.sb_partial_workspace_bytes(p) == 18 * 16 * 5120 * 4
+    assert sb.sb_partial_workspace_bytes(p) == ZERO + 18 * 16 * 5120 * 4
     # ragged: 1000 + 1025 rows -> 1 + 2 chunks; N = 130 -> row stride 132
     p = fake_partial(B=3, N=130, lane_k=(0, 1000, 2025), ldx=1032, ldw=136)
-    assert sb.sb_partial_workspace_bytes(p) == (3 * 3 * 132 * 4 + 255) // 256 * 256
+    assert sb.sb_partial_workspace_bytes(p) == ZERO + up256(3 * 3 * 132 * 4)
     assert sb.sb_partial_workspace_bytes(fake_partial(B=0)) == 0
 
 
