@@ -1100,22 +1100,29 @@ __device__ __forceinline__ int x_swz(int r, int j)
 
 struct LargeGrid {
     int mblocks;  // ceil(B / 256)
-    int mpx;      // m-blocks per XCD slot (mblocks >= 8) or 0 (plain order)
+    int mpx;      // groups of 8 m-blocks (mblocks >= 8) or 0 (plain order)
     int nblocks;  // total 256-column blocks over all lanes
 };
 
-// Workgroup id -> (m-block, n-block).  With at least 8 m-blocks, XCD slot
-// x = id % 8 (workgroups are handed to the XCDs round-robin) takes m-blocks
-// x, x+8, ... and walks the n-blocks in order, so every XCD keeps its X rows
-// in its own L2 and all XCDs stream the same weight block at about the same
-// time.  With fewer m-blocks the m-blocks of one n-block are consecutive.
-// A placement hint only: any bijection gives the same results.
+// n-blocks per super-tile of the XCD-aware order.
+constexpr int kSuperN = 4;
+
+// Workgroup id -> (m-block, n-block).  With at least 8 m-blocks the blocks
+// are grouped into super-tiles of 8 m-blocks x kSuperN n-blocks, 32
+// workgroups: as many as an XCD has CUs.  XCD x = id % 8 (workgroups are
+// handed to the XCDs round-robin) takes super-tiles x, x+8, ..., so the 32
+// workgroups an XCD runs at a time read each K stage's 8 hidden-row slabs
+// and kSuperN weight slabs through its own L2: 384 KB per stage from beyond
+// the L2 instead of the 1.06 MB that 32 n-blocks of one m-block need.  With
+// fewer m-blocks the m-blocks of one n-block are consecutive.  A placement
+// hint only: any bijection gives the same results.
 __device__ __forceinline__ bool large_block(const LargeGrid &g, int id, int &mb, int &nb)
 {
     if (g.mpx > 0) {
         const int xcd = id & 7, local = id >> 3;
-        mb = (local % g.mpx) * 8 + xcd;
-        nb = local / g.mpx;
+        const int st = (local / (8 * kSuperN)) * 8 + xcd, w = local % (8 * kSuperN);
+        mb = (st % g.mpx) * 8 + w % 8;
+        nb = (st / g.mpx) * kSuperN + w / 8;
     } else {
         mb = id % g.mblocks;
         nb = id / g.mblocks;
@@ -1372,7 +1379,8 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
     int64_t nwg;
     if (g.mblocks >= 8) {
         g.mpx = (g.mblocks + 7) / 8;
-        nwg = (int64_t)8 * g.mpx * g.nblocks;
+        const int64_t supers = (int64_t)g.mpx * ((g.nblocks + kSuperN - 1) / kSuperN);
+        nwg = ((supers + 7) / 8) * 8 * (8 * kSuperN);
     } else {
         g.mpx = 0;
         nwg = (int64_t)g.mblocks * g.nblocks;
