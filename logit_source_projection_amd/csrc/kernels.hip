@@ -1100,29 +1100,40 @@ __device__ __forceinline__ int x_swz(int r, int j)
 
 struct LargeGrid {
     int mblocks;  // ceil(B / 256)
-    int mpx;      // groups of 8 m-blocks (mblocks >= 8) or 0 (plain order)
+    int sm;       // m-blocks per super-tile (8, 4 or 2), or 0 for the plain order
     int nblocks;  // total 256-column blocks over all lanes
 };
 
-// n-blocks per super-tile of the XCD-aware order.
-constexpr int kSuperN = 4;
+// Workgroups per super-tile of the XCD-aware order: as many as an XCD has CUs.
+constexpr int kSuperWG = 32;
 
-// Workgroup id -> (m-block, n-block).  With at least 8 m-blocks the blocks
-// are grouped into super-tiles of 8 m-blocks x kSuperN n-blocks, 32
-// workgroups: as many as an XCD has CUs.  XCD x = id % 8 (workgroups are
-// handed to the XCDs round-robin) takes super-tiles x, x+8, ..., so the 32
-// workgroups an XCD runs at a time read each K stage's 8 hidden-row slabs
-// and kSuperN weight slabs through its own L2: 384 KB per stage from beyond
-// the L2 instead of the 1.06 MB that 32 n-blocks of one m-block need.  With
-// fewer m-blocks the m-blocks of one n-block are consecutive.  A placement
-// hint only: any bijection gives the same results.
+// Super-tile rows for a batch of `mblocks` 256-row blocks: 8 from 8 m-blocks
+// up, 4 or 2 for exactly that many, else 0 (plain order).  Timed with
+// bench.py on batches of 1 to 8 m-blocks: the super-tiles gained 2-5 % at 2
+// and 4 m-blocks, lost up to 1.5 % at 3, and grouping 3, 5, 6 or 7 m-blocks
+// into half-empty groups of 2 or 4 lost 15-28 %.
+inline __host__ __device__ int super_rows(int mblocks)
+{
+    return mblocks >= 8 ? 8 : (mblocks == 4 || mblocks == 2 ? mblocks : 0);
+}
+
+// Workgroup id -> (m-block, n-block).  The blocks form super-tiles of sm
+// m-blocks x kSuperWG / sm n-blocks (8 x 4 from 8 m-blocks up).  XCD x = id
+// % 8 (workgroups are handed to the XCDs round-robin) takes super-tiles x,
+// x+8, ..., so the 32 workgroups an XCD runs at a time read each K stage's
+// hidden-row and weight slabs through its own L2: with 8 x 4, 384 KB per
+// stage from beyond the L2 instead of the 1.06 MB that 32 n-blocks of one
+// m-block need.  Without super-tiles the m-blocks of one n-block are
+// consecutive.  A placement hint only: any bijection gives the same results.
 __device__ __forceinline__ bool large_block(const LargeGrid &g, int id, int &mb, int &nb)
 {
-    if (g.mpx > 0) {
+    if (g.sm > 0) {
+        const int sn = kSuperWG / g.sm;
+        const int mgroups = (g.mblocks + g.sm - 1) / g.sm;
         const int xcd = id & 7, local = id >> 3;
-        const int st = (local / (8 * kSuperN)) * 8 + xcd, w = local % (8 * kSuperN);
-        mb = (st % g.mpx) * 8 + w % 8;
-        nb = (st / g.mpx) * kSuperN + w / 8;
+        const int st = (local / kSuperWG) * 8 + xcd, w = local % kSuperWG;
+        mb = (st % mgroups) * g.sm + w % g.sm;
+        nb = (st / mgroups) * sn + w / g.sm;
     } else {
         mb = id % g.mblocks;
         nb = id / g.mblocks;
@@ -1377,12 +1388,13 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
     for (int i = 0; i < a.lanes.k; ++i)
         g.nblocks += (a.lanes.off[i + 1] - a.lanes.off[i] + a.lanes.shift[i] + kLBN - 1) / kLBN;
     int64_t nwg;
-    if (g.mblocks >= 8) {
-        g.mpx = (g.mblocks + 7) / 8;
-        const int64_t supers = (int64_t)g.mpx * ((g.nblocks + kSuperN - 1) / kSuperN);
-        nwg = ((supers + 7) / 8) * 8 * (8 * kSuperN);
+    g.sm = super_rows(g.mblocks);
+    if (g.sm > 0) {
+        const int sn = kSuperWG / g.sm;
+        const int64_t supers =
+            (int64_t)((g.mblocks + g.sm - 1) / g.sm) * ((g.nblocks + sn - 1) / sn);
+        nwg = ((supers + 7) / 8) * 8 * kSuperWG;
     } else {
-        g.mpx = 0;
         nwg = (int64_t)g.mblocks * g.nblocks;
     }
     const size_t lds = (size_t)kLLdsBytes;

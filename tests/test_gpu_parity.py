@@ -57,6 +57,7 @@ SMALL = [
     (256, 96, 1536, [0, 512, 1024, 1536], False),
     (300, 200, 3000, [0, 1000, 1001, 2999, 3000], True),
     (513, 72, 777, [0, 300, 777], True),
+    (1000, 40, 1400, [0, 704, 1400], False),   # four m-blocks: super-tiles of 4 x 8
     (2100, 40, 520, [0, 256, 520], False),
 ]
 
