@@ -39,7 +39,9 @@
  *
  * Ownership and threading
  *  - The caller allocates every device buffer.  The library allocates no
- *    device memory, keeps no state between calls and is thread-safe.
+ *    device memory and is thread-safe.  The only thing it keeps between
+ *    calls is a per-device note that it has raised two kernels' LDS limits
+ *    (hipFuncSetAttribute, once per device).
  *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
  *    the default stream).  Inputs are read-only.  The workspace is scratch
  *    owned by the call until its work completes on the stream; calls that

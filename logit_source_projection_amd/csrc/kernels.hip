@@ -33,6 +33,8 @@
 //     two tiles.
 #include "kernels.h"
 
+#include <atomic>
+
 #include <float.h>
 #include <limits.h>
 
@@ -72,6 +74,24 @@ __device__ __forceinline__ u32x4 load16w(__amdgpu_buffer_rsrc_t r, uint32_t voff
 }
 
 // (value, index) order: larger value first, then lower index.
+// Raises a kernel's dynamic-LDS limit on the current device, once per device
+// (the attribute is held per device; devices past 63 set it on every call).
+// Concurrent first calls may both set it, which is harmless.
+static hipError_t raise_lds_limit(const void *kernel, int bytes, std::atomic<uint64_t> &done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit))
+        return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit)
+        done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2)
 {
     return v1 > v2 || (v1 == v2 && i1 < i2);
@@ -1398,14 +1418,10 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
         nwg = (int64_t)g.mblocks * g.nblocks;
     }
     const size_t lds = (size_t)kLLdsBytes;
-    static bool attr_set = false;  // idempotent; a race only repeats the call
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)head_gemm_large_kernel<EPI>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_done{0};
+    const hipError_t e = raise_lds_limit((const void *)head_gemm_large_kernel<EPI>, (int)lds, lds_done);
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(head_gemm_large_kernel<EPI>, dim3((unsigned)nwg), dim3(kLThreads), lds, s,
                        a, g);
     return hipGetLastError();
@@ -1699,15 +1715,10 @@ hipError_t launch_normalize(float *lp, int64_t ld, const float *lse, int32_t B, 
 {
     if (B <= 0 || V <= 0)
         return hipSuccess;
-    static bool attr_set = false;  // idempotent; a race only repeats the call
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)normalize_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           kNormLdsBytes);
-        if (e != hipSuccess)
-            return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_done{0};
+    const hipError_t e = raise_lds_limit((const void *)normalize_kernel, kNormLdsBytes, lds_done);
+    if (e != hipSuccess)
+        return e;
     dim3 grid((V + kNormCols - 1) / kNormCols, B);
     hipLaunchKernelGGL(normalize_kernel, grid, dim3(kThreads), kNormLdsBytes, s, lp, ld, lse, V);
     return hipGetLastError();
