@@ -123,7 +123,7 @@ def record_traffic(args):
     """Scale the call's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the
     same counters read for the plain copy of known size run in the same
     process, and store the bytes per call in the traffic file.  A head call
-    below 256 rows is one head_gemm_kernel launch; the partial-completion
+    of at most 128 rows is one head-GEMM launch; the partial-completion
     call is the partial GEMM plus the lane reduction, whose per-dispatch
     averages are added."""
     from logit_source_projection_amd import inputs
@@ -440,7 +440,7 @@ def main():
     rows_s = B / (ms * 1e-3)
     nbytes = algorithmic_bytes(d, args.surface)
     achieved = nbytes / (ms * 1e-3) / 1e9
-    one_launch = B < 256 and args.surface in ("tokens", "logprobs")
+    one_launch = B <= 128 and args.surface in ("tokens", "logprobs")  # no combine kernel
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4),
                     traffic=recorded_traffic(args.workload, args.surface, B),

@@ -48,7 +48,7 @@
  *    share one workspace must be ordered on one stream.
  *  - A workspace must be ZERO-FILLED before its first use (allocate it once,
  *    zeroed, and reuse it).  Every workspace starts with the same fixed
- *    region (140,032 bytes) of completion counters, per-lane result keys and
+ *    region (74,496 bytes) of completion counters, per-lane result keys and
  *    per-tile slice counters.  Calls read it only where it is zero on entry
  *    and leave it zero when they complete, and no call writes anything else
  *    there, so one workspace (sized for the largest call) stays valid for
@@ -141,8 +141,8 @@ size_t sb_workspace_bytes(const sb_head_desc *desc, int surface, sb_status *stat
  * ids[b] = lowest global index of max_v z[b][v].  Each lane reduces to one
  * (max, lowest-index) result per row inside the GEMM epilogue; the per-lane
  * results are combined in ascending lane order.  The full logits are never
- * written to memory.  One kernel launch for B < 256 (the last workgroup of a
- * row group writes the IDs); for B >= 256 the GEMM and a combine kernel.
+ * written to memory.  One kernel launch for B <= 128 (the last workgroup of
+ * a row group writes the IDs); for B > 128 the GEMM and a combine kernel.
  *   ids  DEVICE int32 [B]
  *   ws   DEVICE workspace of >= sb_workspace_bytes(desc, SB_SURF_TOKENS)
  *        bytes, 16-byte aligned

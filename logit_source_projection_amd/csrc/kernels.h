@@ -130,9 +130,12 @@ inline int slice_steps(int H, int slices)
 // through the completion protocol.
 hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s);
 
-// Batches of at least this many rows use the large-batch (MFMA-bound) head
-// GEMM for every surface.
-constexpr int kLargeBatch = 256;
+// Batches of at least this many rows (more than two 64-row groups) use the
+// large-batch (MFMA-bound) head GEMM for every surface.  bench.py timings of
+// both kernels from 65 to 768 rows: the pair kernel is faster up to 128 rows
+// (0.37 against 0.40-0.41 ms on the MoE head at 128), the large kernel from
+// 144 rows on (0.40-0.42 against 0.45 ms at 144, 0.44 against 0.57 ms at 255).
+constexpr int kLargeBatch = 129;
 
 // Large-batch head GEMM: writes the (row, tile) results (and logits /
 // shards) only; ids / lse / sel_lp come from launch_combine afterwards.

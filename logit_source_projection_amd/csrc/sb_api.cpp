@@ -20,7 +20,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Every workspace starts with the same fixed region that must be zero on
 // entry and that every call leaves zero: completion counters (row groups x
-// lanes), per-lane keys (rows x lanes, for B < 256) and per-tile slice
+// lanes), per-lane keys (rows x lanes, for B <= 128) and per-tile slice
 // counters.  Its size does not depend on the call, so no call -- of any
 // shape, surface or entry point -- writes non-zero data where a later call
 // expects zeros.
@@ -36,7 +36,7 @@ constexpr size_t kZeroSlices =
 constexpr size_t kZeroBytes =
     (kZeroSlices + sbk::kMaxSplitTiles * sizeof(uint32_t) + kRegionAlign - 1) / kRegionAlign *
     kRegionAlign;
-static_assert(kZeroBytes == 140032, "the size include/sb.h states for the zeroed region");
+static_assert(kZeroBytes == 74496, "the size include/sb.h states for the zeroed region");
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -75,13 +75,13 @@ def up256(n):
 
 
 # Every workspace starts with one fixed zeroed region, whatever the call:
-# completion counters for up to 4 row groups x 65, per-lane keys for up to
-# 255 rows x 64 lanes (8 B each), then 2048 per-tile slice counters.
-ZERO = up256(up256(up256(4 * 65 * 4) + 255 * 64 * 8) + 2048 * 4)
+# completion counters for up to 2 row groups x 65, per-lane keys for up to
+# 128 rows x 64 lanes (8 B each), then 2048 per-tile slice counters.
+ZERO = up256(up256(up256(2 * 65 * 4) + 128 * 64 * 8) + 2048 * 4)
 
 
 def test_workspace_bytes_for_the_workloads():
-    assert ZERO == 140032
+    assert ZERO == 74496
     h = fake_head(B=16, H=5120, V=151936, off=(0, 37984, 75968, 113952, 151936))
     # tile capacity per lane: ceil((37984 + 56) / 128), room for a lane grid
     # shifted by up to 56 columns onto a cache-line boundary

@@ -97,7 +97,7 @@ def test_lane_base_alignment(require_gpu, B):
         np.testing.assert_allclose(g["lse"], ref["lse"], rtol=4e-7, atol=0)
 
 
-@pytest.mark.parametrize("B", [16, 17, 32, 33, 64, 65, 255, 256, 257])
+@pytest.mark.parametrize("B", [16, 17, 32, 33, 64, 65, 128, 129, 255, 256, 257])
 def test_batch_boundaries(require_gpu, B):
     """Both sides of every switch on the batch size: one, two and four row
     blocks per workgroup, several row groups, the large-batch kernel."""

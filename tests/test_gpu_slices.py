@@ -22,7 +22,7 @@ from tests.test_gpu_partial import upload as upload_partial
 pytestmark = pytest.mark.gpu
 
 # Workspace bytes every call reserves up front (the fixed zeroed region).
-ZERO = 140032
+ZERO = 74496
 
 
 def slices_of(head, B):
@@ -116,10 +116,11 @@ def test_one_workspace_for_every_shape_surface_and_entry_point(require_gpu):
     calls = [
         ("tokens", 3, 256, 1000, 1),
         ("full", 40, 512, 6000, 8),
+        ("logprobs", 128, 512, 3000, 5),  # two row groups of the pair kernel
         ("tokens", 64, 2048, 3000, 16),   # split, 16 lanes
         ("logprobs", 20, 640, 9000, 3),
         ("partial", 16, 0, 520, 2),
-        ("tokens", 255, 136, 4000, 64),   # four row groups, 64 lanes
+        ("tokens", 255, 136, 4000, 64),   # large-batch kernel, 64 lanes
         ("logprobs", 64, 4096, 2048, 2),  # split
         ("tokens", 1, 5120, 9000, 1),     # split
         ("full", 300, 72, 1000, 4),       # large-batch kernel
