@@ -47,6 +47,8 @@ SPLIT = [
     (40, 2056, 777, [0, 300, 777], True, 4),          # four row blocks; slices of 20, 20, 20, 5 steps
     (64, 4096, 2048, [0, 1024, 2048], False, 8),
     (7, 3000, 5000, [0, 2500, 5000], True, 5),        # 94 steps: 20, 20, 20, 20, 14
+    (16, 2048, 8192, list(range(0, 8193, 128)), True, 4),  # 64 lanes of one or two tiles each
+    (64, 8192, 2000, [0, 1000, 2000], True, 8),       # 256 steps: 8 slices of 32
 ]
 
 
