@@ -26,9 +26,9 @@
  *    global index wins (section 3.1: a projection operator declares
  *    deterministic tie-breaking).
  *  - Logits are fp32 sums of exact bf16 x bf16 products.  The order in which
- *    each logit is accumulated depends only on (B, H), never on the surface,
- *    the lane split or the column position, so the three calls return
- *    bit-identical logits and IDs for the same inputs.
+ *    each logit is accumulated depends only on (B, H, V), never on the
+ *    surface, the lane split or the column position, so the three calls
+ *    return bit-identical logits and IDs for the same inputs.
  *  - lse is an online sum over 128-column tiles.  A lane's tile grid starts on
  *    the cache line that holds the lane's first column, so lse (and sel_lp and
  *    the complete log-probs) can differ in the last bits between shard

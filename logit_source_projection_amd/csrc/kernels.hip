@@ -22,8 +22,9 @@
 //   * K steps of 32 rows are interleaved over the 4 waves (wave w takes steps
 //     w, w+4, ...); every wave keeps its own fp32 accumulators and the four
 //     partial tiles are added in wave order 0+1+2+3 through LDS.  Each logit
-//     is therefore accumulated in an order fixed by H alone, independent of
-//     the lane split, the column position and the epilogue;
+//     is therefore accumulated in an order fixed by H alone (by B, H and V
+//     for a head split into K slices), independent of the lane split, the
+//     column position and the epilogue;
 //   * buffer loads with per-step rebased resources: rows beyond H and
 //     columns beyond the lane's end read as zero without faulting;
 //   * weight loads are non-temporal when one row group covers the batch
