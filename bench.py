@@ -272,6 +272,25 @@ class Runner:
         return start.elapsed_time(stop) / steps
 
 
+def copy_ceiling_gbs(torch, mib=1024, reps=5):
+    """A measured streaming ceiling beside the published peak: the rate of a
+    plain 1 GiB device-to-device copy, counting the bytes read and written."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2 * (mib << 20) / (ms * 1e-3) / 1e9
+
+
 CPU_SECONDS = 10.0
 
 
@@ -491,6 +510,11 @@ def main():
             x=hashlib.sha256(d["x"].tobytes()).hexdigest()[:16],
             w=hashlib.sha256(d["w"].tobytes()).hexdigest()[:16])
         report["input_gen_s"] = round(gen_s, 2)
+        if roofline["bound"] == "hbm":
+            ceil = copy_ceiling_gbs(torch)
+            report["copy_ceiling"] = dict(
+                gbs=round(ceil, 1), what="device copy of 1 GiB (torch copy_), read + write bytes",
+                frac=round(achieved / ceil, 4))
 
     cpu = None
     if not args.no_cpu_baseline:
