@@ -261,3 +261,13 @@ def test_partial_output_and_workspace_checks():
     assert partial_status(p, ws=FAKE + 4) == sb.SB_ERR_ALIGN
     # an empty batch is a valid no-op that touches nothing
     assert partial_status(fake_partial(B=0), out=None, ws=None, ws_bytes=0) == sb.SB_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libsb.so every call raises; nothing falls back to another path."""
+    monkeypatch.setattr(sb, "_lib", None)
+    monkeypatch.setattr(sb, "LIB_PATH", str(tmp_path / "libsb.so"))
+    with pytest.raises(RuntimeError, match="libsb.so not found"):
+        sb.lib()
+    with pytest.raises(RuntimeError, match="libsb.so not found"):
+        sb.sb_workspace_bytes(fake_head(), sb.SB_SURF_TOKENS)
