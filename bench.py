@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dense_decode",
                     choices=["tiny", "dense_decode", "moe_decode", "large_vocab", "prefill",
-                             "mlp_down"],
+                             "dense_share", "mlp_down"],
                     help="mlp_down times sb_partial_complete (the row-parallel MLP down "
                          "projection) instead of the head")
     ap.add_argument("--op", default="sum", choices=["sum", "prod", "min", "max"],
@@ -198,7 +198,14 @@ class Runner:
         self.stream = stream
         dev = torch.device("cuda:0")
         self.x = sb.to_device_bf16(d["x"], dev)
-        self.w = sb.to_device_bf16(d["w"], dev)
+        w = sb.to_device_bf16(d["w"], dev)
+        ldw = d.get("ldw", d["V"])
+        if ldw != d["V"]:
+            # the shard's rows at the workload's row stride
+            wp = torch.zeros((d["H"], ldw), dtype=w.dtype, device=dev)
+            wp[:, :d["V"]] = w
+            w = wp[:, :d["V"]]
+        self.w = w
         self.head = sb.Head(self.x, self.w, d["lane_off"])
         B, V = d["B"], d["V"]
         self.ids = torch.empty(B, dtype=torch.int32, device=dev)

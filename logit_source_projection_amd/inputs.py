@@ -129,7 +129,15 @@ WORKLOADS = {
     "moe_decode": (64, 4096, 151936, 2, 0.02, True),
     "large_vocab": (16, 6144, 200064, 4, 0.015, False),
     "prefill": (2048, 5120, 151936, 4, 0.02, False),
+    # one GPU's lane of the dense head when it is sharded over 4 GPUs
+    "dense_share": (16, 5120, 37984, 1, 0.02, False),
 }
+
+# Weight row stride (elements) where it is not V: the dense share's rows are
+# padded to 76,032 bytes (an odd multiple of 256), as a deployment would lay
+# out one GPU's shard; its own width puts every other row 64 bytes into a
+# cache line.
+WORKLOAD_LDW = {"dense_share": 38016}
 
 TINY_TIE_ROW = 1
 TINY_TIE_COLS = (1000, 3000)
@@ -195,7 +203,7 @@ def make_workload(name, seed=0, B=None, w=None):
             plant_near_tie(x, w, r, a, b)
             planted.append((r, a, b))
     return dict(name=name, x=x, w=w, lane_off=lane_off, B=B, H=H, V=V, k=k,
-                planted=planted)
+                planted=planted, ldw=WORKLOAD_LDW.get(name, V))
 
 
 def make_random(B, H, V, lane_off, seed=0, sigma_x=1.0, sigma_w=0.02):

@@ -57,3 +57,14 @@ def test_large_vocab_with_planted_near_ties(require_gpu, B):
 def test_prefill_sampled_rows(require_gpu):
     rows = [0, 1, 15, 16, 63, 64, 511, 1023, 1024, 1500, 2046, 2047]
     run_workload("prefill", rows=rows)
+
+
+def test_dense_share(require_gpu):
+    """One GPU's lane of the dense head (sharded over 4 GPUs), at the padded
+    row stride a deployment uses, with NaN bits in the padding."""
+    d = inputs.make_workload("dense_share")
+    assert d["ldw"] == 38016
+    print(f"workload dense_share B={d['B']} H={d['H']} V={d['V']} ldw={d['ldw']}", flush=True)
+    g = run_surfaces(upload(d, lanes_separate=True, pad_w=d["ldw"] - d["V"]))
+    check_internal(g)
+    check_against_oracle(g, oracle.logits(d["x"], d["w"]), d["lane_off"])
