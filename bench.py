@@ -123,12 +123,19 @@ def record_traffic(args):
     """Scale the call's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the
     same counters read for the plain copy of known size run in the same
     process, and store the bytes per call in the traffic file.  A head call
-    of at most 128 rows is one head-GEMM launch; the partial-completion
-    call is the partial GEMM plus the lane reduction, whose per-dispatch
-    averages are added."""
+    of at most 128 rows is one head-GEMM launch, preceded for 33-64 rows by
+    the hidden-row pack; the partial-completion call is the partial GEMM plus
+    the lane reduction.  The per-dispatch averages of a call's kernels are
+    added."""
     from logit_source_projection_amd import inputs
-    kernel_tags = ("partial_gemm", "partial_reduce") if args.workload == "mlp_down" \
-        else ("head_gemm",)
+    d = (inputs.PARTIAL_WORKLOADS if args.workload == "mlp_down" else inputs.WORKLOADS)[args.workload]
+    B = args.B if args.B is not None else d[0]
+    if args.workload == "mlp_down":
+        kernel_tags = ("partial_gemm", "partial_reduce")
+    elif 32 < B <= 64:
+        kernel_tags = ("pack_hidden", "head_gemm")
+    else:
+        kernel_tags = ("head_gemm",)
     calib = args.copy_calibration_mib << 20
     if calib <= 0:
         sys.exit("--record-traffic needs the --copy-calibration-mib of the profiled run")
@@ -155,8 +162,6 @@ def record_traffic(args):
                           factor=round(factor, 5), bytes=int(round(kib * 1024.0 * factor)))
     if rec["fetch"]["kernel"] != rec["write"]["kernel"]:
         sys.exit("the two passes name different head kernels")
-    d = (inputs.PARTIAL_WORKLOADS if args.workload == "mlp_down" else inputs.WORKLOADS)[args.workload]
-    B = args.B if args.B is not None else d[0]
     if args.workload == "mlp_down":
         args.surface = args.op
     try:
@@ -467,11 +472,16 @@ def main():
     nbytes = algorithmic_bytes(d, args.surface)
     achieved = nbytes / (ms * 1e-3) / 1e9
     one_launch = B <= 128 and args.surface in ("tokens", "logprobs")  # no combine kernel
+    if one_launch and 32 < B <= 64:
+        kernel = "whole call: hidden-row pack (1 MB) + head_gemm_kernel"
+    elif one_launch:
+        kernel = "head_gemm_kernel (the whole call is this one launch)"
+    else:
+        kernel = "whole call (head GEMM and its follow-up kernels)"
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4),
                     traffic=recorded_traffic(args.workload, args.surface, B),
-                    kernel=("head_gemm_kernel (the whole call is this one launch)" if one_launch
-                            else "whole call (head GEMM and its follow-up kernels)"),
+                    kernel=kernel,
                     algorithmic_bytes=nbytes)
     if args.workload == "prefill":
         tf = flops(d) / (ms * 1e-3) / 1e12

@@ -141,8 +141,10 @@ size_t sb_workspace_bytes(const sb_head_desc *desc, int surface, sb_status *stat
  * ids[b] = lowest global index of max_v z[b][v].  Each lane reduces to one
  * (max, lowest-index) result per row inside the GEMM epilogue; the per-lane
  * results are combined in ascending lane order.  The full logits are never
- * written to memory.  One kernel launch for B <= 128 (the last workgroup of
- * a row group writes the IDs); for B > 128 the GEMM and a combine kernel.
+ * written to memory.  One head kernel launch for B <= 128 (the last
+ * workgroup of a row group writes the IDs), preceded for 33 <= B <= 64 by a
+ * copy of x into the workspace in fragment order; for B > 128 the GEMM and a
+ * combine kernel.
  *   ids  DEVICE int32 [B]
  *   ws   DEVICE workspace of >= sb_workspace_bytes(desc, SB_SURF_TOKENS)
  *        bytes, 16-byte aligned

@@ -71,7 +71,18 @@ struct HeadArgs {
     int32_t slice_steps;         // kStepK-row steps per slice, a multiple of kWaves
     float *kpart;                // [T][kslices][rows per group][kTileN] fp32 partial tiles
     uint32_t *kctr;              // [T] per-tile slice counters: zero on entry, left zero
+    // Hidden rows packed per K step for 33-64 rows (one row group of four
+    // blocks): [steps][4][64 lanes] 16-byte units, written by the call.
+    uint16_t *xp;
 };
+
+// Bytes of the packed hidden rows of a call (0 where X is read directly).
+inline size_t packed_hidden_bytes(int B, int H)
+{
+    return (B > 2 * kRowBlock && B <= kRowBlock * kMaxMB && H > 0)
+               ? (size_t)((H + kStepK - 1) / kStepK) * kMaxMB * 1024
+               : 0;
+}
 
 // Tiles of a lane of vi columns whose grid starts `shift` columns early.
 inline int lane_tiles(int vi, int shift) { return (vi + shift + kTileN - 1) / kTileN; }

@@ -143,7 +143,9 @@ struct Frags {
     u32x4 x[MB];
 };
 
-template <int MB, int POL>
+// XP: xbase holds the hidden rows packed per step (pack_hidden_kernel), MB KB
+// per step, and xvo[mb] = (64 mb + lane) * 16.
+template <int MB, int POL, bool XP = false>
 __device__ __forceinline__ void load_step(Frags<MB> &f, const uint16_t *wbase, int64_t wbytes,
                                           const uint16_t *xbase, int64_t xbytes, int k0,
                                           int64_t ldw, const uint32_t (&wvo)[8],
@@ -152,7 +154,8 @@ __device__ __forceinline__ void load_step(Frags<MB> &f, const uint16_t *wbase, i
     // Resources rebased to this step's first hidden row: offsets stay small.
     const int64_t wshift = (int64_t)k0 * ldw;
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + wshift, wbytes - wshift * 2);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + k0, xbytes - (int64_t)k0 * 2);
+    const int64_t xshift = XP ? (int64_t)(k0 / kStepK) * (MB * 512) : k0;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + xshift, xbytes - xshift * 2);
 #pragma unroll
     for (int r = 0; r < 8; ++r)
         f.w[r] = load16w<POL>(rw, wvo[r]);
@@ -459,12 +462,41 @@ __device__ __forceinline__ void emit_tile_row(const HeadArgs &a, const float (&y
     }
 }
 
+// The hidden rows of one row group (MB blocks of 16 rows) packed per 32-deep
+// step: unit (s, mb, lane) holds X[16 mb + lane % 16][32 s + 8 (lane / 16)
+// .. + 7] (zeros past B rows and past H), so that a wave's fragment load of
+// a step reads MB contiguous KB instead of 16 half cache lines per row block.
+// Positions past H in a row are never read.
+template <int MB>
+__global__ __launch_bounds__(MB * 64) void pack_hidden_kernel(const uint16_t *x, int64_t ldx,
+                                                              int B, int H, uint16_t *xp)
+{
+    const int s = blockIdx.x;
+    const int mb = threadIdx.x >> 6, L = threadIdx.x & 63;
+    const int row = kRowBlock * mb + (L & 15);
+    const int k0 = kStepK * s + 8 * (L >> 4);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < B) {
+        const uint16_t *p = x + (int64_t)row * ldx + k0;
+        if (k0 + 8 <= H) {
+            v = *reinterpret_cast<const u32x4 *>(p);  // 16-byte aligned: ldx % 8 == 0
+        } else if (k0 < H) {
+            uint16_t e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                e[j] = k0 + j < H ? p[j] : (uint16_t)0;
+            v = __builtin_bit_cast(u32x4, e);
+        }
+    }
+    reinterpret_cast<u32x4 *>(xp)[(int64_t)s * (MB * 64) + threadIdx.x] = v;
+}
+
 template <int MB>
 struct Occupancy {
     static constexpr int kBlocksPerCU = MB == 1 ? 1 : (MB == 2 ? 3 : 2);
 };
 
-template <int MB, int EPI, int POL>
+template <int MB, int EPI, int POL, bool XP>
 __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_gemm_kernel(const HeadArgs a)
 {
     __shared__ float red[kWaves][kRowBlock][kTileN + 4];
@@ -504,8 +536,11 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
     const int64_t wcols = ((int64_t)(Vi - cb) + 7) & ~(int64_t)7;
     const int64_t wbytes = H > 0 ? (((int64_t)(H - 1) * a.ldw) + wcols) * 2 : 0;
     const int rows_here = min(a.B - m0, kRowBlock * MB);
-    const uint16_t *xbase = a.x + (int64_t)m0 * a.ldx;
-    const int64_t xbytes = H > 0 ? (((int64_t)(rows_here - 1) * a.ldx) + ((H + 7) & ~7)) * 2 : 0;
+    // hidden rows: from X itself, or (XP, one row group) packed per step
+    const uint16_t *xbase = XP ? a.xp : a.x + (int64_t)m0 * a.ldx;
+    const int64_t xbytes =
+        XP ? (int64_t)((H + kStepK - 1) / kStepK) * (MB * 1024)
+           : (H > 0 ? (((int64_t)(rows_here - 1) * a.ldx) + ((H + 7) & ~7)) * 2 : 0);
 
     uint32_t wvo[8];
 #pragma unroll
@@ -514,7 +549,8 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
     uint32_t xvo[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-        xvo[mb] = (uint32_t)(((int64_t)(kRowBlock * mb + n) * a.ldx + 8 * g) * 2);
+        xvo[mb] = XP ? (uint32_t)((64 * mb + L) * 16)
+                     : (uint32_t)(((int64_t)(kRowBlock * mb + n) * a.ldx + 8 * g) * 2);
 
     f32x4 acc[MB][8];
 #pragma unroll
@@ -535,13 +571,13 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
     Frags<MB> fa, fb;
     int k0 = (s_begin + wave) * kStepK;
     if (nw > 0)
-        load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, k0, a.ldw, wvo, xvo);
+        load_step<MB, POL, XP>(fa, wbase, wbytes, xbase, xbytes, k0, a.ldw, wvo, xvo);
     for (int i = 0; i + 2 <= nw; i += 2) {
-        load_step<MB, POL>(fb, wbase, wbytes, xbase, xbytes, k0 + kWaves * kStepK, a.ldw, wvo,
+        load_step<MB, POL, XP>(fb, wbase, wbytes, xbase, xbytes, k0 + kWaves * kStepK, a.ldw, wvo,
                            xvo);
         compute_step<MB>(fa, acc, k0, H, g);
         if (i + 2 < nw)
-            load_step<MB, POL>(fa, wbase, wbytes, xbase, xbytes, k0 + 2 * kWaves * kStepK, a.ldw,
+            load_step<MB, POL, XP>(fa, wbase, wbytes, xbase, xbytes, k0 + 2 * kWaves * kStepK, a.ldw,
                                wvo, xvo);
         compute_step<MB>(fb, acc, k0 + kWaves * kStepK, H, g);
         k0 += 2 * kWaves * kStepK;
@@ -1428,24 +1464,34 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int MB, int POL>
+template <int MB, int POL, bool XP = false>
 hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
 {
     const int rpg = kRowBlock * MB;
     const int ntiles = a.lanes.tile0[a.lanes.k];
     dim3 grid(((ntiles + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg) * a.kslices);
+    if constexpr (XP) {
+        const int nsteps = (a.H + kStepK - 1) / kStepK;
+        if (nsteps > 0) {
+            hipLaunchKernelGGL(pack_hidden_kernel<MB>, dim3(nsteps), dim3(MB * 64), 0, s, a.x,
+                               a.ldx, a.B, a.H, a.xp);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+    }
     switch (epi) {
     case kEpiPair:
-        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPair, POL>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPair, POL, XP>), grid, dim3(kThreads), 0, s, a);
         break;
     case kEpiPairLse:
-        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPairLse, POL>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPairLse, POL, XP>), grid, dim3(kThreads), 0, s, a);
         break;
     case kEpiPairLseOut:
-        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPairLseOut, POL>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiPairLseOut, POL, XP>), grid, dim3(kThreads), 0, s, a);
         break;
     case kEpiShard:
-        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiShard, POL>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((head_gemm_kernel<MB, kEpiShard, POL, XP>), grid, dim3(kThreads), 0, s, a);
         break;
     default:
         return hipErrorInvalidValue;
@@ -1682,7 +1728,7 @@ hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s)
         // One row group streams each weight tile once; with several row
         // groups two tiles per workgroup share the hidden rows.
         if (a.B <= kRowBlock * kMaxMB)
-            return launch_mb<kMaxMB, kPolicyStream>(a, epi, s);
+            return launch_mb<kMaxMB, kPolicyStream, true>(a, epi, s);
         return launch_pair<kPolicyShared>(a, epi, s);
     }
 }

@@ -94,7 +94,7 @@ struct Layout {
     int nchunks = 0;      // full-logit argmax chunks per row
     int groups = 0;       // row groups (grid y) of the head GEMM
     int kslices = 1;      // K slices of the head GEMM (one row group only)
-    size_t sync = 0, keys = 0, kctr = 0, kpart = 0, pair = 0, mse = 0, lane_mse = 0;
+    size_t sync = 0, keys = 0, kctr = 0, kpart = 0, xp = 0, pair = 0, mse = 0, lane_mse = 0;
     size_t shard[SB_MAX_LANES] = {}, partial = 0;
     size_t total = 0;
 };
@@ -125,6 +125,11 @@ Layout layout(const sb_head_desc *d, int surface)
         L.kpart = at;
         at = align_up(at + (size_t)L.T * L.kslices * rpg * sbk::kTileN * sizeof(float),
                       kRegionAlign);
+    }
+    if (const size_t xpb = sbk::packed_hidden_bytes(d->B, d->H)) {
+        // the hidden rows packed per K step (33-64 rows)
+        L.xp = at;
+        at = align_up(at + xpb, kRegionAlign);
     }
     switch (surface) {
     case SB_SURF_TOKENS:
@@ -215,15 +220,19 @@ void fill_args(const sb_head_desc *d, const Layout &L, sbk::HeadArgs &a)
     a.slice_steps = sbk::slice_steps(d->H, L.kslices);
     a.kpart = nullptr;
     a.kctr = nullptr;
+    a.xp = nullptr;
 }
 
-// The K-slice regions of a split head (a no-op without a split).
+// The K-slice regions of a split head and the packed hidden rows of 33-64
+// rows (each a no-op where the call has none).
 void set_slices(const Layout &L, void *ws, sbk::HeadArgs &a)
 {
     if (L.kslices > 1) {
         a.kpart = region<float>(ws, L.kpart);
         a.kctr = region<uint32_t>(ws, L.kctr);
     }
+    if (L.xp)
+        a.xp = region<uint16_t>(ws, L.xp);
 }
 
 sb_status check_ws(const Layout &L, void *ws, size_t ws_bytes)

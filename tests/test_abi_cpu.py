@@ -108,14 +108,16 @@ def test_workspace_bytes_of_a_split_head():
     # the split depends on (B, H, V), not on the lane split
     h4 = fake_head(B=16, H=5120, V=8192, off=(0, 2048, 4096, 6144, 8192))
     assert sb.sb_workspace_bytes(h4, sb.SB_SURF_TOKENS) == ZERO + 4 * 17 * 4 * 16 * 128 * 4
-    # 127 tiles: 3 slices (of 56, 56 and 48 steps); 64 rows: 64-row partial tiles
+    # 127 tiles: 3 slices (of 56, 56 and 48 steps); 64 rows: 64-row partial tiles,
+    # then the hidden rows packed per 32-deep step (4 row blocks x 64 lanes x 16 B)
     h = fake_head(B=64, H=5120, V=16256, off=(0, 16256))
-    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == ZERO + 128 * 3 * 64 * 128 * 4
+    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == \
+        ZERO + 128 * 3 * 64 * 128 * 4 + 160 * 4096
     # one GPU's lane of the dense head (297 tiles) and of the MoE head: no split
     assert sb.sb_workspace_bytes(fake_head(B=16, H=5120, V=37984, off=(0, 37984)),
                                  sb.SB_SURF_TOKENS) == ZERO
     assert sb.sb_workspace_bytes(fake_head(B=64, H=4096, V=75968, off=(0, 75968)),
-                                 sb.SB_SURF_TOKENS) == ZERO
+                                 sb.SB_SURF_TOKENS) == ZERO + 128 * 4096
     # fewer than 32 hidden steps (H <= 992): never split
     assert sb.sb_workspace_bytes(fake_head(B=16, H=992, V=1024, off=(0, 1024)),
                                  sb.SB_SURF_TOKENS) == ZERO

@@ -25,15 +25,17 @@ pytestmark = pytest.mark.gpu
 ZERO = 74496
 
 
-def slices_of(head, B):
+def slices_of(head, B, H):
     """K slices of a head, read back from its token workspace size: past the
-    zeroed region, each slice holds one fp32 partial tile (rows per group x
-    128 columns) per tile of the tile capacity (lanes sized for the largest
-    cache-line shift of 56 columns)."""
+    zeroed region (and, for 33-64 rows, the hidden rows packed per 32-deep
+    step, 4 KB per step), each slice holds one fp32 partial tile (rows per
+    group x 128 columns) per tile of the tile capacity (lanes sized for the
+    largest cache-line shift of 56 columns)."""
     rpg = 16 if B <= 16 else (32 if B <= 32 else 64)
     T = sum((head.lane_off[i + 1] - head.lane_off[i] + 56 + 127) // 128
             for i in range(len(head.lane_off) - 1))
-    extra = sb.sb_workspace_bytes(head, sb.SB_SURF_TOKENS) - ZERO
+    packed = (H + 31) // 32 * 4096 if 32 < B <= 64 else 0
+    extra = sb.sb_workspace_bytes(head, sb.SB_SURF_TOKENS) - ZERO - packed
     assert extra % (T * rpg * 128 * 4) == 0
     return max(1, extra // (T * rpg * 128 * 4))
 
@@ -57,7 +59,7 @@ def test_split_heads(require_gpu, B, H, V, off, sep, S):
     print(f"split B={B} H={H} V={V} off={off} S={S}", flush=True)
     d = inputs.make_random(B, H, V, off, seed=B + H + V)
     head = upload(d, lanes_separate=sep, pad_x=(8 - H % 8) % 8 + 8)
-    assert slices_of(head, B) == S
+    assert slices_of(head, B, H) == S
     g = run_surfaces(head)
     check_internal(g)
     check_against_oracle(g, oracle.logits(d["x"], d["w"]), d["lane_off"])
