@@ -28,7 +28,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="dense_decode",
                     choices=["tiny", "dense_decode", "moe_decode", "large_vocab", "prefill",
                              "dense_share", "mlp_down"],
@@ -303,6 +303,22 @@ def copy_ceiling_gbs(torch, mib=1024, reps=5):
     return 2 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
+def library_gemm_ms(torch, x, w, reps=10):
+    """Context beside the roofline: the vendor library's plain product of the
+    same operands (bf16 output, no epilogue) on torch's current stream."""
+    y = torch.matmul(x, w)
+    torch.matmul(x, w, out=y)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        torch.matmul(x, w, out=y)
+    b.record()
+    torch.cuda.synchronize()
+    del y
+    return a.elapsed_time(b) / reps
+
+
 CPU_SECONDS = 10.0
 
 
@@ -527,6 +543,11 @@ def main():
             x=hashlib.sha256(d["x"].tobytes()).hexdigest()[:16],
             w=hashlib.sha256(d["w"].tobytes()).hexdigest()[:16])
         report["input_gen_s"] = round(gen_s, 2)
+        lib_ms = library_gemm_ms(torch, run.x, run.w)
+        report["library_gemm"] = dict(
+            ms=round(lib_ms, 4), ratio=round(ms / lib_ms, 4),
+            what="torch.matmul of x [B, H] by w [H, V], bf16 in and out (the vendor GEMM "
+                 "library), the product alone: no argmax, no logsumexp; ratio = this call / it")
         if roofline["bound"] == "hbm":
             ceil = copy_ceiling_gbs(torch)
             report["copy_ceiling"] = dict(
