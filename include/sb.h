@@ -56,8 +56,9 @@
  *    included.
  *  - A head of fewer than 128 vocabulary tiles of 128 columns (B <= 64) splits
  *    each tile's hidden sum into up to 8 slices that run as separate
- *    workgroups; the slice partials are added in slice order.  The split
- *    depends on (B, H, V) only, so the guarantees above still hold.
+ *    workgroups, and one of 257 to 352 tiles (B <= 16, H >= 4065) into 2;
+ *    the slice partials are added in slice order.  The split depends on
+ *    (B, H, V) only, so the guarantees above still hold.
  *
  * Errors
  *  - Validation is synchronous: on any error status nothing is enqueued and

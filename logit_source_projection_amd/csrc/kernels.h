@@ -101,17 +101,26 @@ inline int rows_per_group(int B)
 // leaves most of the 256 CUs idle.  Such a head splits every tile's hidden
 // steps into slices of at least kMinSliceSteps steps, up to kMaxSlices of
 // them, so that about kSplitTarget workgroups (one per CU) run.  Larger heads
-// are not split: one workgroup per tile streamed fastest from 128 tiles up in
-// timings of 1 to 8 slices (a split adds a partial-tile write and a fold per
-// slice).  The split depends on (B, H, V) only -- not on the lane split or
-// the shard placement -- so every surface and every lane split of a head sums
-// each logit in the same order.
+// are not split, except just past one tile per CU (below): one workgroup per
+// tile streamed fastest from 128 tiles up in timings of 1 to 8 slices (a
+// split adds a partial-tile write and a fold per slice).  The split depends
+// on (B, H, V) only -- not on the lane split or the shard placement -- so
+// every surface and every lane split of a head sums each logit in the same
+// order.
 constexpr int kSplitBelowTiles = 128;
 constexpr int kSplitTarget = 256;
 constexpr int kMinSliceSteps = 16;
 constexpr int kMaxSlices = 8;
+// Just past one tile per CU (kSplitTarget < tiles <= kSplitPairMaxTiles),
+// one 16-row block and at least kSplitPairMinSteps hidden steps: two slices
+// per tile, so that no CU streams two whole tiles while others idle (timed
+// at H = 5120: 4-7 % faster from 264 to 320 tiles, 1 % at 352, slower at
+// 256 and from 391 tiles on).
+constexpr int kSplitPairMaxTiles = 352;
+constexpr int kSplitPairMinSteps = 128;
 constexpr int kMaxSplitTiles = 2048;  // tile capacity of the slice counters
-static_assert(kSplitBelowTiles + 2 * kMaxLanes <= kMaxSplitTiles,
+static_assert(kSplitBelowTiles + 2 * kMaxLanes <= kMaxSplitTiles &&
+                  kSplitPairMaxTiles + 2 * kMaxLanes <= kMaxSplitTiles,
               "a split head's tiles, shifted lanes included, fit the counters");
 inline int k_slices(int B, int H, int V)
 {
@@ -119,11 +128,17 @@ inline int k_slices(int B, int H, int V)
         return 1;
     const int tiles = (V + kTileN - 1) / kTileN;
     const int nsteps = (H + kStepK - 1) / kStepK;
-    if (tiles >= kSplitBelowTiles)
+    int s;
+    if (tiles < kSplitBelowTiles) {
+        s = (kSplitTarget + tiles - 1) / tiles;
+        s = s < kMaxSlices ? s : kMaxSlices;
+        s = s < nsteps / kMinSliceSteps ? s : nsteps / kMinSliceSteps;
+    } else if (B <= kRowBlock && tiles > kSplitTarget && tiles <= kSplitPairMaxTiles &&
+               nsteps >= kSplitPairMinSteps) {
+        s = 2;
+    } else {
         return 1;
-    int s = (kSplitTarget + tiles - 1) / tiles;
-    s = s < kMaxSlices ? s : kMaxSlices;
-    s = s < nsteps / kMinSliceSteps ? s : nsteps / kMinSliceSteps;
+    }
     if (s <= 1)
         return 1;
     // whole multiples of kWaves steps per slice, and no empty slice

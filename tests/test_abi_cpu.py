@@ -113,9 +113,16 @@ def test_workspace_bytes_of_a_split_head():
     h = fake_head(B=64, H=5120, V=16256, off=(0, 16256))
     assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == \
         ZERO + 128 * 3 * 64 * 128 * 4 + 160 * 4096
-    # one GPU's lane of the dense head (297 tiles) and of the MoE head: no split
+    # one GPU's lane of the dense head (297 tiles, just past one tile per CU,
+    # 16 rows): 2 slices of 80 steps, partial tiles for the 298 tiles of capacity
     assert sb.sb_workspace_bytes(fake_head(B=16, H=5120, V=37984, off=(0, 37984)),
-                                 sb.SB_SURF_TOKENS) == ZERO
+                                 sb.SB_SURF_TOKENS) == ZERO + 298 * 2 * 16 * 128 * 4
+    # ... but not at 17 rows, at H = 2048 (64 steps), at 256 or at 353 tiles
+    for kw in (dict(B=17, H=5120, V=37984), dict(B=16, H=2048, V=37984),
+               dict(B=16, H=5120, V=256 * 128), dict(B=16, H=5120, V=353 * 128)):
+        assert sb.sb_workspace_bytes(fake_head(off=(0, kw["V"]), **kw),
+                                     sb.SB_SURF_TOKENS) == ZERO, kw
+    # one GPU's lane of the MoE head (594 tiles): the packed hidden rows only
     assert sb.sb_workspace_bytes(fake_head(B=64, H=4096, V=75968, off=(0, 75968)),
                                  sb.SB_SURF_TOKENS) == ZERO + 128 * 4096
     # fewer than 32 hidden steps (H <= 992): never split

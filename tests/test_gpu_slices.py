@@ -51,6 +51,12 @@ SPLIT = [
     (7, 3000, 5000, [0, 2500, 5000], True, 5),        # 94 steps: 20, 20, 20, 20, 14
     (16, 2048, 8192, list(range(0, 8193, 128)), True, 4),  # 64 lanes of one or two tiles each
     (64, 8192, 2000, [0, 1000, 2000], True, 8),       # 256 steps: 8 slices of 32
+    # just past one tile per CU at 16 rows: two slices
+    (16, 5120, 37984, [0, 37984], False, 2),          # one GPU's lane of the dense head
+    (9, 4100, 40000, [0, 20000, 40000], True, 2),     # 313 tiles; 129 steps: 68 + 61, K tail
+    (16, 4096, 45056, [0, 45056], False, 2),          # 352 tiles
+    (16, 4096, 45184, [0, 45184], False, 1),          # 353 tiles: not split
+    (17, 5120, 37984, [0, 37984], False, 1),          # two row blocks: not split
 ]
 
 
