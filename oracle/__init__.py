@@ -27,14 +27,14 @@ Readings taken where the pages are silent:
   to the lowest global vocabulary index;
 * log-probabilities are log-softmax of the raw logits (no temperature, bias or
   soft-cap); the selected-token log-probability belongs to the argmax token;
-* the argmax decision is taken on the logits rounded to float32 (the GPU
-  path's logit precision; the pages name none); the fp64 decision is returned
-  beside it for reporting;
-* a row is a "near tie" when its fp64 top-2 gap is below 2e-3 * max_v |z|.
+* the argmax is decided on the fp64 logits themselves (the plain definition);
+* a row is a "near tie" when its fp64 top-2 gap (largest logit minus the
+  next largest, over distinct indices) is below 2e-3 * max_v |z|.
 
 Parity pins: every function here is pinned in ``tests/test_oracle_*.py`` by
-exact-rational brute force, closed forms and invariants; none is "parity
-unpinned".
+exact-rational brute force, closed forms, invariants and planted mistakes --
+top2_gap and the near-tie flag included (exact gaps on every row of the
+tiny heads, rows planted just above, at and just below the threshold).
 """
 import ctypes
 import os
@@ -128,80 +128,83 @@ def check_lanes(lane_off, V):
     return off
 
 
-def lane_pairs(z, lane_off, decide_dtype=np.float32):
+def lane_pairs(z, lane_off):
     """Per-lane projection on every row (SemBridge section 6 / Figure 1:
     argmax runs once per lane, "argmax x k", and each lane yields one result).
 
-    For lane i = [off_i, off_{i+1}) and each row b:
-      M_i[b]  = max over the lane (in decide_dtype, the decision precision)
+    For lane i = [off_i, off_{i+1}) and each row b, all in fp64:
+      M_i[b]  = max over the lane
       A_i[b]  = smallest global index in the lane attaining M_i[b]
-      mf_i[b] = fp64 max over the lane
-      S_i[b]  = sum over the lane of exp(z - mf_i) in fp64
-    Returns arrays of shape [B, k]: M, A, mf, S.
+      S_i[b]  = sum over the lane of exp(z - M_i)
+    Returns arrays of shape [B, k]: M, A, S.
     """
     B, V = z.shape
     off = check_lanes(lane_off, V)
     k = len(off) - 1
-    zd = z.astype(decide_dtype)
-    M = np.empty((B, k), dtype=decide_dtype)
+    M = np.empty((B, k), dtype=np.float64)
     A = np.empty((B, k), dtype=np.int64)
-    mf = np.empty((B, k), dtype=np.float64)
     S = np.empty((B, k), dtype=np.float64)
     for i in range(k):
-        seg_d = zd[:, off[i]:off[i + 1]]
         seg = z[:, off[i]:off[i + 1]]
         # np.argmax returns the first occurrence of the maximum: lowest index.
-        a = np.argmax(seg_d, axis=1)
+        a = np.argmax(seg, axis=1)
         A[:, i] = off[i] + a
-        M[:, i] = seg_d[np.arange(B), a]
-        mf[:, i] = seg.max(axis=1)
-        S[:, i] = np.exp(seg - mf[:, i:i + 1]).sum(axis=1)
-    return M, A, mf, S
+        M[:, i] = seg[np.arange(B), a]
+        S[:, i] = np.exp(seg - M[:, i:i + 1]).sum(axis=1)
+    return M, A, S
 
 
-def combine(M, A, mf, S):
+def combine(M, A, S):
     """Fold the per-lane results in ascending lane order (one int32 result per
     lane is what source projection ships, SemBridge section 6).
 
-      id  = A_j for the first lane j whose M_j equals max_i M_i
-      lse = m + log(sum_i S_i * exp(mf_i - m)),  m = max_i mf_i
+      id  = A_j for the first lane j whose M_j equals m = max_i M_i
+      lse = m + log(sum_i S_i * exp(M_i - m))
     Returns (ids int64 [B], lse float64 [B]).
     """
     B, k = M.shape
-    best = M.max(axis=1)
-    j = np.argmax(M == best[:, None], axis=1)  # first lane holding the max
+    m = M.max(axis=1)
+    j = np.argmax(M == m[:, None], axis=1)  # first lane holding the max
     ids = A[np.arange(B), j]
-    m = mf.max(axis=1)
-    lse = m + np.log((S * np.exp(mf - m[:, None])).sum(axis=1))
+    lse = m + np.log((S * np.exp(M - m[:, None])).sum(axis=1))
     return ids, lse
 
 
-def full_logit_argmax(z, lane_off, decide_dtype=np.float32):
+def full_logit_argmax(z, lane_off):
     """The full-logit plan inside the oracle (SemBridge section 5.2): the lane
     shards are reconstructed into the complete [B, V] tensor (the
     destination-local AllGather) and a plain first-occurrence argmax runs on
     it."""
     off = check_lanes(lane_off, z.shape[1])
     shards = [z[:, off[i]:off[i + 1]] for i in range(len(off) - 1)]
-    full = np.concatenate(shards, axis=1).astype(decide_dtype)
+    full = np.concatenate(shards, axis=1)
     return np.argmax(full, axis=1).astype(np.int64)
 
 
 def top2_gap(z):
-    """Largest minus second-largest logit of each row (0 for an exact tie)."""
+    """Per row, the largest logit minus the second largest, where the two are
+    taken at distinct indices: z_(1) - z_(2) >= 0, and 0 for an exact tie.
+    np.partition with kth = V - 2 leaves the two largest entries of the row in
+    its last two slots, the larger last.  +inf for a one-column row."""
     if z.shape[1] < 2:
         return np.full(z.shape[0], np.inf)
     top = np.partition(z, -2, axis=1)[:, -2:]
     return top[:, 1] - top[:, 0]
 
 
-def project(z, lane_off, decide_dtype=np.float32):
+def near_tie(z, gap):
+    """Rows whose top-2 gap lies strictly below NEAR_TIE_REL * max_v |z|: their
+    IDs may differ between fp32 and fp64 logits, so they are reported rather
+    than compared."""
+    return gap < NEAR_TIE_REL * np.abs(z).max(axis=1)
+
+
+def project(z, lane_off):
     """Token and log-probability surfaces from fp64 logits z [B, V].
 
     Returns a dict with
-      ids       int64 [B]  argmax token IDs, lowest index on ties, decided in
-                           decide_dtype (float32: the GPU's logit precision)
-      ids_f64   int64 [B]  the same decision taken in float64 (reporting)
+      ids       int64 [B]  argmax token IDs over the fp64 logits, lowest index
+                           on ties
       lse       float64 [B] logsumexp of each row
       sel_lp    float64 [B] log-probability of the argmax token
       lane_max, lane_arg, lane_sumexp   per-lane results, [B, k]
@@ -210,21 +213,16 @@ def project(z, lane_off, decide_dtype=np.float32):
     and checks the pages' invariant that the full-logit plan yields the same
     IDs as per-lane projection (Figure 1 caption; section 6.3).
     """
-    M, A, mf, S = lane_pairs(z, lane_off, decide_dtype)
-    ids, lse = combine(M, A, mf, S)
-    r0 = full_logit_argmax(z, lane_off, decide_dtype)
+    M, A, S = lane_pairs(z, lane_off)
+    ids, lse = combine(M, A, S)
+    r0 = full_logit_argmax(z, lane_off)
     if not np.array_equal(ids, r0):
         raise AssertionError("oracle: per-lane projection differs from the full-logit argmax")
-    M64, A64, _, _ = lane_pairs(z, lane_off, np.float64)
-    ids64, _ = combine(M64, A64, mf, S)
-    # The selected token is the argmax token; its logit is the row maximum in
-    # fp64 terms when the fp32 and fp64 decisions agree.
     sel = z[np.arange(z.shape[0]), ids]
     gap = top2_gap(z)
-    near = gap < NEAR_TIE_REL * np.abs(z).max(axis=1)
-    return dict(ids=ids, ids_f64=ids64, lse=lse, sel_lp=sel - lse,
-                lane_max=M, lane_arg=A, lane_sumexp=S, lane_maxf=mf,
-                gap=gap, near_tie=near)
+    return dict(ids=ids, lse=lse, sel_lp=sel - lse,
+                lane_max=M, lane_arg=A, lane_sumexp=S,
+                gap=gap, near_tie=near_tie(z, gap))
 
 
 def logprobs(z, lse):

@@ -16,6 +16,8 @@ import pytest
 
 import oracle
 from logit_source_projection_amd import inputs
+from fractions import Fraction
+
 from tests.exact import bf16_to_fraction, exact_argmax, exact_logits
 
 
@@ -48,12 +50,83 @@ def pin_ids_exact(logits_fn, project_fn, x, w, lane_off):
     r = project_fn(z, lane_off)
     ze = exact_logits(x, w)
     for b in range(x.shape[0]):
-        assert int(r["ids_f64"][b]) == exact_argmax(ze[b]), b
-        # with these magnitudes the fp32 decision agrees unless the exact gap
-        # is below float32 resolution
+        assert int(r["ids"][b]) == exact_argmax(ze[b]), b
+
+
+def _fp64_bound(x, w, b):
+    """Largest error bound over row b of an fp64 sum of H exact products."""
+    H = x.shape[1]
+    xs = [abs(bf16_to_fraction(x[b, h])) for h in range(H)]
+    worst = 0
+    for v in range(w.shape[1]):
+        mag = sum(xs[h] * abs(bf16_to_fraction(w[h, v])) for h in range(H))
+        worst = max(worst, mag)
+    return float(worst) * H * 2.0 ** -52
+
+
+def pin_gap_exact(logits_fn, project_fn, x, w, lane_off):
+    """top2_gap and near_tie on every row against the exact rationals: the gap
+    is the largest exact logit minus the next largest (distinct indices), and
+    the flag is gap < 2e-3 * max |z| unless the exact gap sits within the fp64
+    error of the threshold."""
+    z = logits_fn(x, w)
+    r = project_fn(z, lane_off)
+    ze = exact_logits(x, w)
+    for b in range(x.shape[0]):
         srt = sorted(ze[b], reverse=True)
-        if float(srt[0] - srt[1]) > 1e-5 * float(abs(srt[0])) or srt[0] == srt[1]:
-            assert int(r["ids"][b]) == exact_argmax(ze[b]), b
+        gap = srt[0] - srt[1]
+        tol = 2 * _fp64_bound(x, w, b) + 1e-300
+        assert abs(float(r["gap"][b]) - float(gap)) <= tol, (b, r["gap"][b], float(gap))
+        thr = Fraction(oracle.NEAR_TIE_REL) * max(abs(q) for q in ze[b])
+        if abs(float(gap - thr)) > 2 * tol:
+            assert bool(r["near_tie"][b]) == (gap < thr), (b, float(gap), float(thr))
+
+
+def threshold_head():
+    """One-hot rows (z[b, :] = W[h_b, :] exactly) whose top-2 gaps sit just
+    below, exactly at and just above the near-tie threshold.  Column 7 holds
+    -500 in every row, so max |z| = 500 and the threshold is 2e-3 * 500 = 1.0
+    (exact in fp64); the rows' largest logits are 4.0.
+
+      row 0: 4.0 vs 3.015625           gap 0.984375  -> near tie
+      row 1: 4.0 vs 2.984375           gap 1.015625  -> not a near tie
+      row 2: 4.0 vs 3.0                gap 1.0 (at)  -> not a near tie (strict)
+      row 3: 4.0 vs 4.0                gap 0         -> near tie
+      row 4: 500 vs 4.0 (no -500)      gap 496       -> not a near tie
+    Rows 0-2 also hold a third value 2.5 (gap to the largest 1.5 > 1), so a
+    gap taken to the third largest would misclassify row 0.
+    Returns (x, w, off, expected gaps, expected flags)."""
+    H, V = 8, 48
+    rng = np.random.default_rng(77)
+    w32 = (rng.standard_normal((H, V)) * 0.02).astype(np.float32)
+    w = inputs.f32_to_bf16_bits(w32)
+    x = np.zeros((5, H), dtype=np.uint16)
+    def bits(v):
+        return np.uint16(inputs.f32_to_bf16_bits(np.array([v], dtype=np.float32))[0])
+    one = bits(1.0)
+    top = [(3.015625, 2.5), (2.984375, 2.5), (3.0, 2.5), (4.0, None)]
+    for b, (second, third) in enumerate(top):
+        x[b, b] = one
+        w[b, 7] = bits(-500.0)
+        w[b, 11] = bits(4.0)
+        w[b, 40] = bits(second)
+        if third is not None:
+            w[b, 25] = bits(third)
+    x[4, 4] = one
+    w[4, 30] = bits(500.0)
+    w[4, 31] = bits(4.0)
+    gaps = [0.984375, 1.015625, 1.0, 0.0, 496.0]
+    flags = [True, False, False, True, False]
+    return x, w, [0, 16, 48], gaps, flags
+
+
+def pin_near_tie_threshold(logits_fn, project_fn):
+    x, w, off, gaps, flags = threshold_head()
+    z = logits_fn(x, w)
+    r = project_fn(z, off)
+    for b, (gp, fl) in enumerate(zip(gaps, flags)):
+        assert float(r["gap"][b]) == gp, (b, r["gap"][b], gp)
+        assert bool(r["near_tie"][b]) == fl, (b, r["near_tie"][b], fl)
 
 
 def pin_lse_mp(logits_fn, project_fn, x, w, lane_off):
@@ -91,6 +164,26 @@ def test_ids_match_exact_argmax(B, H, V, off, seed):
     pin_ids_exact(oracle.logits, oracle.project, x, w, off)
 
 
+@pytest.mark.parametrize("B,H,V,off,seed", TINY_CASES)
+def test_top2_gap_and_near_tie_match_exact_rationals(B, H, V, off, seed):
+    x, w = tiny_head(B, H, V, seed)
+    pin_gap_exact(oracle.logits, oracle.project, x, w, off)
+
+
+def test_near_tie_threshold_rows():
+    pin_near_tie_threshold(oracle.logits, oracle.project)
+
+
+def test_near_tie_gap_on_planted_ties_and_other_rows():
+    """Exact ties (gap 0) and the other rows of the same head, every row
+    against the exact rationals."""
+    B, H, V = 4, 32, 64
+    x, w = tiny_head(B, H, V, 7)
+    inputs.plant_equal_columns(x, w, 2, (50, 30, 5), 40.0)
+    inputs.plant_equal_columns(x, w, 0, (39, 22), 40.0)
+    pin_gap_exact(oracle.logits, oracle.project, x, w, [0, 20, 41, 64])
+
+
 @pytest.mark.parametrize("B,H,V,off,seed", TINY_CASES[:3])
 def test_lse_matches_high_precision(B, H, V, off, seed):
     x, w = tiny_head(B, H, V, seed)
@@ -109,7 +202,7 @@ def test_exact_ties_go_to_lowest_index():
     ze = exact_logits(x, w)
     r = oracle.project(z, off)
     assert ze[2][5] == ze[2][30] == ze[2][50] == max(ze[2])
-    assert int(r["ids"][2]) == 5 and int(r["ids_f64"][2]) == 5
+    assert int(r["ids"][2]) == 5
     assert ze[0][22] == ze[0][39] == max(ze[0])
     assert int(r["ids"][0]) == 22
     assert r["gap"][2] == 0.0 and r["near_tie"][2]
@@ -135,7 +228,7 @@ def test_zero_row_closed_form():
 def test_one_hot_row_selects_weight_row():
     B, H, V = 4, 40, 777
     x, w = tiny_head(B, H, V, 12, sigma_w=0.02)
-    one = np.uint16(inputs.f32_to_bf16_bits(np.float32(1.0)))
+    one = np.uint16(inputs.f32_to_bf16_bits(np.array([1.0], dtype=np.float32))[0])
     for b, h in enumerate([0, 17, 39, 5]):
         x[b, :] = 0
         x[b, h] = one
@@ -144,7 +237,7 @@ def test_one_hot_row_selects_weight_row():
         wrow = np.array([float(bf16_to_fraction(v)) for v in w[h]])
         assert np.array_equal(z[b], wrow)
         r = oracle.project(z, [0, 100, 500, 777])
-        assert int(r["ids"][b]) == int(np.argmax(wrow.astype(np.float32)))
+        assert int(r["ids"][b]) == int(np.argmax(wrow))
 
 
 def test_power_of_two_scaling_is_exact():
@@ -191,9 +284,10 @@ def test_lane_results_match_global_view():
     r = oracle.project(z, off)
     for b in range(B):
         for i in range(4):
-            seg = z[b, off[i]:off[i + 1]].astype(np.float32)
+            seg = z[b, off[i]:off[i + 1]]
             assert r["lane_arg"][b, i] == off[i] + int(np.argmax(seg))
-        assert r["ids"][b] == int(np.argmax(z[b].astype(np.float32)))
+            assert r["lane_max"][b, i] == seg.max()
+        assert r["ids"][b] == int(np.argmax(z[b]))
 
 
 def test_sampled_rows_equal_full_evaluation():
@@ -270,7 +364,6 @@ def test_mutation_highest_index_tie_break_is_caught():
         last = z.shape[1] - 1 - np.argmax(zz, axis=1)
         r = dict(r)
         r["ids"] = last
-        r["ids_f64"] = last
         return r
     assert _fails(lambda: pin_ids_exact(oracle.logits, bad_project, x, w, MUT_OFF))
 
@@ -282,15 +375,14 @@ def test_mutation_lane_off_by_one_is_caught():
 
     def bad_project(z, off):
         r = dict(oracle.project(z, off))
-        M, A, mf, S = oracle.lane_pairs(z[:, :], off)
+        M, A, S = oracle.lane_pairs(z, off)
         # off-by-one: lane 0 loses its last column
         for b in range(z.shape[0]):
-            seg = z[b, off[0]:off[1] - 1].astype(np.float32)
+            seg = z[b, off[0]:off[1] - 1]
             A[b, 0] = off[0] + int(np.argmax(seg))
             M[b, 0] = seg.max()
-        ids, _ = oracle.combine(M, A, mf, S)
+        ids, _ = oracle.combine(M, A, S)
         r["ids"] = ids
-        r["ids_f64"] = ids
         return r
     assert _fails(lambda: pin_ids_exact(oracle.logits, bad_project, x, w, MUT_OFF))
 
@@ -298,9 +390,62 @@ def test_mutation_lane_off_by_one_is_caught():
 def test_mutation_unscaled_lane_sum_is_caught():
     def bad_project(z, off):
         r = dict(oracle.project(z, off))
-        M, A, mf, S = oracle.lane_pairs(z, off)
-        m = mf.max(axis=1)
+        M, A, S = oracle.lane_pairs(z, off)
+        m = M.max(axis=1)
         r["lse"] = m + np.log(S.sum(axis=1))  # forgot exp(mf_i - m)
         r["sel_lp"] = z.max(axis=1) - r["lse"]
         return r
     assert _fails(lambda: pin_lse_mp(oracle.logits, bad_project, MUT_X, MUT_W, MUT_OFF))
+
+
+# Planted mistakes in the top-2 gap and the near-tie flag.  Each replaces the
+# oracle's gap / flag by a plausible wrong version and must fail a pin.
+def _with_gap(gap_fn, flag_fn=None):
+    def bad_project(z, off):
+        r = dict(oracle.project(z, off))
+        r["gap"] = gap_fn(z)
+        r["near_tie"] = (flag_fn or oracle.near_tie)(z, r["gap"])
+        return r
+    return bad_project
+
+
+def _gap_pins_fail(bad_project):
+    x, w = tiny_head(4, 32, 96, 2)
+    return (_fails(lambda: pin_near_tie_threshold(oracle.logits, bad_project)) and
+            _fails(lambda: pin_gap_exact(oracle.logits, bad_project, x, w, [0, 50, 96])))
+
+
+def test_mutation_swapped_gap_operands_is_caught():
+    def swapped(z):
+        top = np.partition(z, -2, axis=1)[:, -2:]
+        return top[:, 0] - top[:, 1]
+    assert _gap_pins_fail(_with_gap(swapped))
+
+
+def test_mutation_gap_to_third_largest_is_caught():
+    def third(z):
+        top = np.partition(z, -3, axis=1)[:, -3:]
+        return top[:, 2] - top[:, 0]
+    assert _fails(lambda: pin_near_tie_threshold(oracle.logits, _with_gap(third)))
+
+
+def test_mutation_threshold_without_abs_is_caught():
+    def no_abs(z, gap):
+        return gap < oracle.NEAR_TIE_REL * z.max(axis=1)
+    bad = _with_gap(oracle.top2_gap, no_abs)
+    assert _fails(lambda: pin_near_tie_threshold(oracle.logits, bad))
+
+
+def test_mutation_non_strict_threshold_is_caught():
+    def le(z, gap):
+        return gap <= oracle.NEAR_TIE_REL * np.abs(z).max(axis=1)
+    bad = _with_gap(oracle.top2_gap, le)
+    assert _fails(lambda: pin_near_tie_threshold(oracle.logits, bad))
+
+
+@pytest.mark.parametrize("factor", [2e-4, 2e-2])
+def test_mutation_wrong_threshold_factor_is_caught(factor):
+    def wrong(z, gap):
+        return gap < factor * np.abs(z).max(axis=1)
+    bad = _with_gap(oracle.top2_gap, wrong)
+    assert _fails(lambda: pin_near_tie_threshold(oracle.logits, bad))
