@@ -43,17 +43,17 @@
  *    calls is a per-device note that it has raised two kernels' LDS limits
  *    (hipFuncSetAttribute, once per device).
  *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
- *    the default stream).  Inputs are read-only.  The workspace is scratch
- *    owned by the call until its work completes on the stream; calls that
- *    share one workspace must be ordered on one stream.
- *  - A workspace must be ZERO-FILLED before its first use (allocate it once,
- *    zeroed, and reuse it).  Every workspace starts with the same fixed
- *    region (74,496 bytes) of completion counters, per-lane result keys and
- *    per-tile slice counters.  Calls read it only where it is zero on entry
- *    and leave it zero when they complete, and no call writes anything else
- *    there, so one workspace (sized for the largest call) stays valid for
- *    later calls of any shape, surface or entry point, partial completion
- *    included.
+ *    the default stream).  Inputs are read-only.
+ *  - The workspace is scratch owned by the call until its work completes on
+ *    the stream: its contents on entry do not matter, and nothing in it is
+ *    valid afterwards.  Every workspace starts with the same fixed region
+ *    (8,192 bytes) of per-tile counters for heads split into K slices (see
+ *    below); a call on a split head clears the counters it uses on `stream`
+ *    before its head kernel runs (by a small clearing launch, or by the
+ *    hidden-row copy for 33 <= B <= 64), so a workspace sized for the
+ *    largest call serves calls of any shape, surface or entry point in any
+ *    order.  Two calls that use one workspace at the same time (on different
+ *    streams without ordering) race and give undefined results.
  *  - A head of fewer than 128 vocabulary tiles of 128 columns (B <= 64) splits
  *    each tile's hidden sum into up to 8 slices that run as separate
  *    workgroups, and one of 257 to 352 tiles (B <= 16, H >= 4065) into 2;
@@ -89,8 +89,9 @@ typedef enum sb_status {
                                 a logits / log-probs leading dim not a
                                 multiple of 4                                  */
     SB_ERR_WORKSPACE = -5,   /* workspace smaller than sb_workspace_bytes()   */
-    SB_ERR_UNSUPPORTED = -6, /* B > 65535, or 40 shard rows or 64 rows of x
-                                span 4 GiB or more                            */
+    SB_ERR_UNSUPPORTED = -6, /* B > 65535; or 40 shard rows or 64 rows of x
+                                span 4 GiB or more; or, for B >= 129, 72
+                                shard rows or 256 rows of x do             */
     SB_ERR_HIP = -7          /* a HIP launch failed                            */
 } sb_status;
 
@@ -142,16 +143,33 @@ size_t sb_workspace_bytes(const sb_head_desc *desc, int surface, sb_status *stat
  * ids[b] = lowest global index of max_v z[b][v].  Each lane reduces to one
  * (max, lowest-index) result per row inside the GEMM epilogue; the per-lane
  * results are combined in ascending lane order.  The full logits are never
- * written to memory.  One head kernel launch for B <= 128 (the last
- * workgroup of a row group writes the IDs), preceded for 33 <= B <= 64 by a
- * copy of x into the workspace in fragment order; for B > 128 the GEMM and a
- * combine kernel.
+ * written to memory.  Launches: the head kernel, which writes one (max,
+ * lowest index) pair per (row, 128-column tile) into the workspace, then a
+ * combine kernel (one workgroup per row) that folds them, lane by lane; for
+ * 33 <= B <= 64 the head kernel is preceded by a copy of x into the
+ * workspace in fragment order, and a head split into K slices by the
+ * clearing of its slice counters (done by that copy where there is one).
  *   ids  DEVICE int32 [B]
  *   ws   DEVICE workspace of >= sb_workspace_bytes(desc, SB_SURF_TOKENS)
  *        bytes, 16-byte aligned
  */
 sb_status sb_project_tokens(const sb_head_desc *desc, int32_t *ids,
                             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Token surface plus each lane's own result (SemBridge Figure 1 caption and
+ * section 5.2: under source projection every lane ships one int32 result per
+ * row).  Same launches and same ids as sb_project_tokens; in addition
+ *   lane_ids[b][i] = lowest global index of the maximum of z[b][v] over lane
+ *                    i's columns (DEVICE int32 [B][k], or NULL)
+ *   lane_max[b][i] = that maximum (DEVICE fp32 [B][k], or NULL; -0 is
+ *                    reported as +0)
+ * ids[b] is lane_ids[b][j] for the first lane j whose lane_max is largest.
+ *   ws  >= sb_workspace_bytes(desc, SB_SURF_TOKENS)
+ */
+sb_status sb_project_lane_results(const sb_head_desc *desc, int32_t *ids,
+                                  int32_t *lane_ids, float *lane_max,
+                                  void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Log-probability surface (SemBridge section 3.2 / 3.4: complete logits plus
@@ -229,8 +247,8 @@ typedef struct sb_partial_desc {
 
 /*
  * Bytes of device workspace sb_partial_complete needs on `desc`: the head
- * calls' fixed zeroed region, which this call leaves untouched, then the fp32
- * chunk partials (no zero-fill needed for this call alone).  0 for B == 0.
+ * calls' fixed counter region, which this call leaves untouched, then the
+ * fp32 chunk partials.  0 for B == 0.
  * Returns 0 and sets *status on an invalid descriptor (statuses as for the
  * head; SB_ERR_LANES for bad lane_k).
  */

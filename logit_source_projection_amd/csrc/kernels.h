@@ -42,6 +42,13 @@ struct LaneTable {
     int32_t k;
 };
 
+// Up to three ranges of 32-bit words that a call clears before its head
+// kernel touches them (the slice counters of a split head).
+struct ZeroRanges {
+    uint32_t *p[3];
+    int32_t n[3];  // words; 0 = unused
+};
+
 struct HeadArgs {
     LaneTable lanes;
     const uint16_t *x;   // bf16 [B][ldx]
@@ -49,20 +56,10 @@ struct HeadArgs {
     int64_t ldw;
     int32_t B, H, V;
     int32_t T;           // row stride of the pair workspaces (>= lanes.tile0[k])
-    int2 *pair;          // [B][T] {float bits of max, global index} (large-batch kernel)
-    float2 *mse;         // [B][T] {tile max, sum exp(y - tile max)}
+    int2 *pair;          // [B][T] {float bits of the tile max, its lowest global index}
+    float2 *mse;         // [B][T] {tile max, sum exp(y - tile max)} (log-prob surfaces)
     float *out;          // [B][ldo] fp32 logits at global columns (kEpiPairLseOut)
     int64_t ldo;
-    // Completion protocol of the token / log-prob surfaces (head_gemm_kernel):
-    // per-lane keys merged by atomic maximum; the workgroup that finishes a
-    // row group's last tile (tokens) or last lane (log-probs) writes ids /
-    // lse / sel_lp.
-    uint32_t *sync;              // [row groups][k + 1] counters: zero on entry, left zero
-    unsigned long long *keys;    // [B][k] per-lane (max, lowest index) keys: zero on entry, left zero
-    float2 *lane_mse;            // [B][k] per-lane {max, sum exp(y - max)}
-    int32_t *ids;        // [B]
-    float *lse;          // [B] or null
-    float *sel_lp;       // [B] or null
     // K slices (head_gemm_kernel, one row group): the hidden steps of every
     // tile are split into kslices contiguous runs of slice_steps steps, one
     // workgroup each; each writes its partial tile to kpart and the last to
@@ -70,10 +67,13 @@ struct HeadArgs {
     int32_t kslices;             // 1 = no split
     int32_t slice_steps;         // kStepK-row steps per slice, a multiple of kWaves
     float *kpart;                // [T][kslices][rows per group][kTileN] fp32 partial tiles
-    uint32_t *kctr;              // [T] per-tile slice counters: zero on entry, left zero
+    uint32_t *kctr;              // [T] per-tile slice counters, cleared before the launch
     // Hidden rows packed per K step for 33-64 rows (one row group of four
     // blocks): [steps][4][64 lanes] 16-byte units, written by the call.
     uint16_t *xp;
+    // Words the head launch needs at zero: cleared by a launch of its own
+    // before the head kernel (by the hidden-row pack for 33-64 rows).
+    ZeroRanges zero;
 };
 
 // Bytes of the packed hidden rows of a call (0 where X is read directly).
@@ -151,9 +151,9 @@ inline int slice_steps(int H, int slices)
     return slices <= 1 ? nsteps : ((nsteps + slices - 1) / slices + kWaves - 1) / kWaves * kWaves;
 }
 
-// Launch the head GEMM with the given epilogue.  For every epilogue except
-// kEpiShard the launch also produces ids (and lse / sel_lp when non-null)
-// through the completion protocol.
+// Launch the head GEMM (B <= 128) with the given epilogue: the (row, tile)
+// pairs (every epilogue but kEpiShard; launch_combine folds them) and the
+// logits or shards.  a.zero is cleared first, on the same stream.
 hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s);
 
 // Batches of at least this many rows (more than two 64-row groups) use the
@@ -162,17 +162,22 @@ hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s);
 // (0.37 against 0.40-0.41 ms on the MoE head at 128), the large kernel from
 // 144 rows on (0.40-0.42 against 0.45 ms at 144, 0.44 against 0.57 ms at 255).
 constexpr int kLargeBatch = 129;
+// Block rows and K stage depth of the large-batch kernel (its 32-bit buffer
+// offsets reach kLargeRows rows of x and kLargeStepK rows of a shard).
+constexpr int kLargeRows = 256;
+constexpr int kLargeStepK = 64;
 
 // Large-batch head GEMM: writes the (row, tile) results (and logits /
-// shards) only; ids / lse / sel_lp come from launch_combine afterwards.
+// shards); ids / lse / sel_lp come from launch_combine afterwards.
 hipError_t launch_head_gemm_large(const HeadArgs &a, int epi, hipStream_t s);
 
-// Fold the (row, tile) workspaces into ids / lse / sel_lp (any may be NULL
-// except ids).  One workgroup per row; tiles folded lane by lane in ascending
-// order, lanes folded in ascending order.
+// Fold the (row, tile) workspaces into ids / lse / sel_lp and the per-lane
+// results lane_ids / lane_max ([B][k]; any may be NULL except ids).  One
+// workgroup per row; tiles folded lane by lane in ascending order, lanes
+// folded in ascending order.
 hipError_t launch_combine(const int2 *pair, const float2 *mse, const LaneTable &lanes,
                           int32_t B, int32_t T, int32_t *ids, float *lse,
-                          float *sel_lp, hipStream_t s);
+                          float *sel_lp, int32_t *lane_ids, float *lane_max, hipStream_t s);
 
 // lp[b][v] -= lse[b] over [B][V] (row stride ld).
 hipError_t launch_normalize(float *lp, int64_t ld, const float *lse, int32_t B,

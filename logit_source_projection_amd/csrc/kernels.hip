@@ -205,196 +205,15 @@ __device__ __forceinline__ void compute_step(Frags<MB> &f, f32x4 (&acc)[MB][8], 
     }
 }
 
-// (value, global index) as one 64-bit key whose unsigned order is value
-// ascending, then index descending: the largest key is the largest value at
-// its lowest index, and merging keys with an atomic maximum gives the same
-// result in any order.  -0 is taken as +0, so equal values always tie.
-__device__ __forceinline__ unsigned long long pack_key(float v, int idx)
-{
-    uint32_t u = __float_as_uint(v);
-    if (u == 0x80000000u)
-        u = 0u;
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)idx);
-}
-
-__device__ __forceinline__ float key_value(unsigned long long key)
-{
-    const uint32_t u = (uint32_t)(key >> 32);
-    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-
-__device__ __forceinline__ int key_index(unsigned long long key)
-{
-    return (int)(0xFFFFFFFFu - (uint32_t)key);
-}
-
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int o, int w)
-{
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, w);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, w);
-    return ((unsigned long long)hi << 32) | lo;
-}
-
-// Threads per row when the workgroup's 256 threads fold `rows` rows: a power
-// of two, at most one wave, so that a row's threads sit in one wave.
-__device__ __forceinline__ int fold_width(int rows)
-{
-    int w = 64;
-    while (w > 1 && w * rows > kThreads)
-        w >>= 1;
-    return w;
-}
-
-// The k lane keys of a row folded into its token ID (and, for the log-prob
-// surfaces, the lane (max, sum-exp) pairs into lse), then the keys cleared.
-// Thread j of a row takes lanes j, j + w, ... in ascending order; the w
-// partial results are combined by a fixed butterfly.
-template <int EPI>
-__device__ void finish_group(const HeadArgs &a, int m0, int rows_here)
-{
-    const int k = a.lanes.k;
-    const int w = fold_width(rows_here);
-    const int r = threadIdx.x / w, j = threadIdx.x % w;
-    const bool rowok = r < rows_here;
-    const int row = m0 + r;
-    unsigned long long best = 0;
-    float m = -INFINITY, se = 0.f;
-    if (rowok) {
-        for (int i = j; i < k; i += w) {
-            unsigned long long *kp = a.keys + (int64_t)row * k + i;
-            const unsigned long long key = __hip_atomic_load(kp, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(kp, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            best = key > best ? key : best;
-            if (EPI != kEpiPair) {
-                const float2 q = a.lane_mse[(int64_t)row * k + i];
-                lse_merge(m, se, q.x, q.y);
-            }
-        }
-    }
-    for (int o = w / 2; o >= 1; o >>= 1) {
-        const unsigned long long ok = shfl_xor_u64(best, o, w);
-        best = ok > best ? ok : best;
-        if (EPI != kEpiPair) {
-            const float om = __shfl_xor(m, o, w);
-            const float os = __shfl_xor(se, o, w);
-            lse_merge(m, se, om, os);
-        }
-    }
-    if (rowok && j == 0) {
-        a.ids[row] = key_index(best);
-        if (EPI != kEpiPair) {
-            const float l = m + __logf(se);
-            if (a.lse)
-                a.lse[row] = l;
-            if (a.sel_lp)
-                a.sel_lp[row] = key_value(best) - l;
-        }
-    }
-}
-
-// Completion protocol, run by every workgroup after its tile's results are
-// published.  Token IDs: every (row, tile) maximum has been merged into the
-// row's key of its lane with an atomic maximum -- the paper's one int32
-// result per lane -- so the workgroup that completes the row group's last
-// tile only folds the k lane keys of each row.  Log-prob surfaces: the
-// (tile max, sum-exp) pairs are written through; the workgroup that
-// completes a lane's last tile folds them in a fixed order into the lane's
-// pair, and the one that completes the last lane folds the lanes.  Counters
-// and keys are left at zero for the next call on the same workspace.
-template <int MB, int EPI>
-__device__ void finish_tile(const HeadArgs &a, int lane, int group, int m0, int rows_here)
-{
-    __shared__ int s_last;
-    const int k = a.lanes.k;
-    uint32_t *lane_ctr = a.sync + (int64_t)group * (k + 1) + lane;
-    uint32_t *group_ctr = a.sync + (int64_t)group * (k + 1) + k;
-
-    wait_all_memory();  // this wave's atomics and written-through results are done
-    __syncthreads();    // ... and every other wave's
-    if (EPI == kEpiPair) {
-        if (threadIdx.x == 0) {
-            const uint32_t old = atomicAdd(group_ctr, 1u);
-            s_last = old == (uint32_t)(a.lanes.tile0[k] - 1);
-        }
-        __syncthreads();
-        if (!s_last)
-            return;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        finish_group<EPI>(a, m0, rows_here);
-        if (threadIdx.x == 0)
-            __hip_atomic_store(group_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
-
-    const int t0 = a.lanes.tile0[lane], t1 = a.lanes.tile0[lane + 1];
-    if (threadIdx.x == 0) {
-        const uint32_t old = atomicAdd(lane_ctr, 1u);
-        s_last = old == (uint32_t)(t1 - t0 - 1);
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
-    // acquire: drop stale cached copies before reading the lane's results
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-    // Thread j of a row merges tiles t0 + j, t0 + j + w, ... in ascending
-    // order (loads issued kFoldBatch at a time: with 64 rows a thread folds
-    // about 150 tiles, and each batch costs one memory round trip), then a
-    // fixed butterfly.
-    {
-        constexpr int kFoldBatch = 32;
-        const int w = fold_width(rows_here);
-        const int r = threadIdx.x / w, j = threadIdx.x % w;
-        const int b = m0 + r;
-        float m = -INFINITY, se = 0.f;
-        if (r < rows_here) {
-            const float2 *row = a.mse + (int64_t)b * a.T;
-            for (int t = t0 + j; t < t1; t += kFoldBatch * w) {
-                float2 q[kFoldBatch];
-#pragma unroll
-                for (int u = 0; u < kFoldBatch; ++u)
-                    q[u] = t + u * w < t1 ? row[t + u * w] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-                for (int u = 0; u < kFoldBatch; ++u)
-                    lse_merge(m, se, q[u].x, q[u].y);
-            }
-        }
-        for (int o = w / 2; o >= 1; o >>= 1) {
-            const float om = __shfl_xor(m, o, w);
-            const float os = __shfl_xor(se, o, w);
-            lse_merge(m, se, om, os);
-        }
-        if (r < rows_here && j == 0)
-            store_through(&a.lane_mse[(int64_t)b * k + lane], __float_as_uint(m),
-                          __float_as_uint(se));
-    }
-    wait_all_memory();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __hip_atomic_store(lane_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t old = atomicAdd(group_ctr, 1u);
-        s_last = old == (uint32_t)(k - 1);
-    }
-    __syncthreads();
-    if (!s_last)
-        return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    finish_group<EPI>(a, m0, rows_here);
-    if (threadIdx.x == 0)
-        __hip_atomic_store(group_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Minimum workgroups per CU handed to the register allocator.  One row block
 // is left unconstrained (it fits 128 registers: 4 waves per SIMD); two row
 // blocks are held to 3 waves per SIMD (168 registers) and four to 2 (256),
 // both without spills.
 // Epilogue of one (row, 128-column tile) for the thread that holds the tile's
 // 8 columns from `colrel` (lane-relative; `gcol` global) of row b: the logits
-// or shard store, the (max, lowest index) key merged into the row's key of its
-// lane, and the written-through (tile max, sum-exp) pair.  The 16 threads of
-// a row are 16 consecutive lanes of one wave.
+// or shard store, and the tile's (max, lowest index) and (tile max, sum-exp)
+// pairs, which the combine launch folds after the head kernel.  The 16
+// threads of a row are 16 consecutive lanes of one wave.
 template <int EPI>
 __device__ __forceinline__ void emit_tile_row(const HeadArgs &a, const float (&y)[8], int b,
                                               bool rowok, int lane, int tile, int colrel,
@@ -453,11 +272,10 @@ __device__ __forceinline__ void emit_tile_row(const HeadArgs &a, const float (&y
                 se += __shfl_xor(se, o, 16);
         }
         if (cg == 0 && rowok) {
-            __hip_atomic_fetch_max(a.keys + (int64_t)b * a.lanes.k + lane, pack_key(bv, bi),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int64_t idx = (int64_t)b * a.T + tile;
+            a.pair[idx] = make_int2(__float_as_int(bv), bi);
             if (EPI != kEpiPair)
-                store_through(&a.mse[(int64_t)b * a.T + tile], __float_as_uint(bv),
-                              __float_as_uint(se));
+                a.mse[idx] = make_float2(bv, se);
         }
     }
 }
@@ -467,10 +285,38 @@ __device__ __forceinline__ void emit_tile_row(const HeadArgs &a, const float (&y
 // .. + 7] (zeros past B rows and past H), so that a wave's fragment load of
 // a step reads MB contiguous KB instead of 16 half cache lines per row block.
 // Positions past H in a row are never read.
+// Zero the call's counters and keys: every thread of the grid takes words
+// i, i + stride, ... of each range.
+__device__ __forceinline__ void clear_ranges(const ZeroRanges &z, int64_t i, int64_t stride)
+{
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+        for (int64_t j = i; j < z.n[r]; j += stride)
+            z.p[r][j] = 0u;
+}
+
+__global__ __launch_bounds__(kThreads) void clear_kernel(const ZeroRanges z)
+{
+    clear_ranges(z, (int64_t)blockIdx.x * kThreads + threadIdx.x, (int64_t)gridDim.x * kThreads);
+}
+
+// Clear the ranges of `z` on stream s (no launch when all are empty).
+hipError_t launch_clear(const ZeroRanges &z, hipStream_t s)
+{
+    const int64_t words = (int64_t)z.n[0] + z.n[1] + z.n[2];
+    if (words <= 0)
+        return hipSuccess;
+    const int64_t wg = (words + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(clear_kernel, dim3((unsigned)(wg < 64 ? wg : 64)), dim3(kThreads), 0, s, z);
+    return hipGetLastError();
+}
+
 template <int MB>
 __global__ __launch_bounds__(MB * 64) void pack_hidden_kernel(const uint16_t *x, int64_t ldx,
-                                                              int B, int H, uint16_t *xp)
+                                                              int B, int H, uint16_t *xp,
+                                                              const ZeroRanges z)
 {
+    clear_ranges(z, (int64_t)blockIdx.x * (MB * 64) + threadIdx.x, (int64_t)gridDim.x * (MB * 64));
     const int s = blockIdx.x;
     const int mb = threadIdx.x >> 6, L = threadIdx.x & 63;
     const int row = kRowBlock * mb + (L & 15);
@@ -648,8 +494,6 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
         if (!s_fold)
             return;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        if (threadIdx.x == 0)
-            __hip_atomic_store(a.kctr + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             if (m0 + kRowBlock * mb >= a.B)
@@ -668,8 +512,6 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
             emit_tile_row<EPI>(a, y, b, b < a.B, lane, tile, colrel, nvalid, gcol0 + 8 * cg, cg);
         }
     }
-    if (EPI != kEpiShard)
-        finish_tile<MB, EPI>(a, lane, group, m0, rows_here);
 }
 
 // ---------------------------------------------------------------------------
@@ -858,11 +700,6 @@ __global__ __launch_bounds__(kThreads, Occupancy<kMaxMB>::kBlocksPerCU) void hea
                                a.lanes.off[lane2[u]] + colrel, cg);
         }
     }
-    if (EPI != kEpiShard) {
-        finish_tile<MB, EPI>(a, lane2[0], group, m0, rows_here);
-        if (second)
-            finish_tile<MB, EPI>(a, lane2[1], group, m0, rows_here);
-    }
 }
 
 template <int POL>
@@ -871,6 +708,9 @@ hipError_t launch_pair(const HeadArgs &a, int epi, hipStream_t s)
     const int rpg = kRowBlock * kMaxMB;
     const int npairs = (a.lanes.tile0[a.lanes.k] + 1) / 2;
     dim3 grid(((npairs + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg));
+    const hipError_t e = launch_clear(a.zero, s);
+    if (e != hipSuccess)
+        return e;
     switch (epi) {
     case kEpiPair:
         hipLaunchKernelGGL((head_gemm_pair_kernel<kEpiPair, POL>), grid, dim3(kThreads), 0, s, a);
@@ -890,33 +730,52 @@ hipError_t launch_pair(const HeadArgs &a, int epi, hipStream_t s)
     return hipGetLastError();
 }
 
-// One workgroup per row: fold the per-tile results lane by lane.
+// One workgroup per row folds the per-(row, tile) results.  Wave w takes
+// lanes w, w + 4, ...; in a lane, thread j merges tiles t0 + j, t0 + j + 64,
+// ... in ascending order (kCombineBatch loads in flight), and a fixed 64-lane
+// butterfly merges the threads.  The lane results are then folded in
+// ascending lane order: the ID of the first lane holding the row maximum
+// (lowest index on ties, since lanes ascend), and
+// lse = M + log sum_i S_i exp(M_i - M).  Every order here is fixed by the
+// tile grid, so lse is reproduced bit for bit.
+constexpr int kCombineBatch = 8;
+
 __global__ __launch_bounds__(kThreads) void combine_kernel(const int2 *pair, const float2 *mse,
                                                            const LaneTable lanes, int T,
                                                            int32_t *ids, float *lse,
-                                                           float *sel_lp)
+                                                           float *sel_lp, int32_t *lane_ids,
+                                                           float *lane_max)
 {
-    __shared__ float wv[kWaves], wm[kWaves], ws[kWaves];
-    __shared__ int wi[kWaves];
+    __shared__ float lv[kMaxLanes], lm[kMaxLanes], ls[kMaxLanes];
+    __shared__ int li[kMaxLanes];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int L = tid & 63, wave = tid >> 6;
-    float rv = -INFINITY, rm = -INFINITY, rs = 0.f;
-    int ri = INT_MAX;
-    for (int lane = 0; lane < lanes.k; ++lane) {
+    const int2 *prow = pair + (int64_t)b * T;
+    const float2 *mrow = mse ? mse + (int64_t)b * T : nullptr;
+    for (int lane = wave; lane < lanes.k; lane += kWaves) {
         const int t0 = lanes.tile0[lane], t1 = lanes.tile0[lane + 1];
         float bv = -INFINITY, m = -INFINITY, s = 0.f;
         int bi = INT_MAX;
-        for (int t = t0 + tid; t < t1; t += kThreads) {
-            const int2 p = pair[(int64_t)b * T + t];
-            const float pv = __int_as_float(p.x);
-            if (better(pv, p.y, bv, bi)) {
-                bv = pv;
-                bi = p.y;
+        for (int t = t0 + L; t < t1; t += 64 * kCombineBatch) {
+            int2 p[kCombineBatch];
+            float2 q[kCombineBatch];
+#pragma unroll
+            for (int u = 0; u < kCombineBatch; ++u) {
+                const int tu = t + 64 * u;
+                p[u] = tu < t1 ? prow[tu] : make_int2(__float_as_int(-INFINITY), INT_MAX);
+                if (mrow)
+                    q[u] = tu < t1 ? mrow[tu] : make_float2(-INFINITY, 0.f);
             }
-            if (mse) {
-                const float2 q = mse[(int64_t)b * T + t];
-                lse_merge(m, s, q.x, q.y);
+#pragma unroll
+            for (int u = 0; u < kCombineBatch; ++u) {
+                const float pv = __int_as_float(p[u].x);
+                if (better(pv, p[u].y, bv, bi)) {
+                    bv = pv;
+                    bi = p[u].y;
+                }
+                if (mrow)
+                    lse_merge(m, s, q[u].x, q[u].y);
             }
         }
 #pragma unroll
@@ -932,39 +791,38 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const int2 *pair, con
             lse_merge(m, s, om, os);
         }
         if (L == 0) {
-            wv[wave] = bv;
-            wi[wave] = bi;
-            wm[wave] = m;
-            ws[wave] = s;
+            lv[lane] = bv + 0.f;  // -0 reported as +0
+            li[lane] = bi;
+            lm[lane] = m;
+            ls[lane] = s;
         }
-        __syncthreads();
-        if (tid == 0) {
-            float lv = -INFINITY, lm = -INFINITY, ls = 0.f;
-            int li = INT_MAX;
-            for (int w = 0; w < kWaves; ++w) {
-                if (better(wv[w], wi[w], lv, li)) {
-                    lv = wv[w];
-                    li = wi[w];
-                }
-                lse_merge(lm, ls, wm[w], ws[w]);
-            }
-            // lanes in ascending order: a later lane wins only if strictly
-            // larger or equal with a lower index (never, indices ascend).
-            if (better(lv, li, rv, ri)) {
-                rv = lv;
-                ri = li;
-            }
-            lse_merge(rm, rs, lm, ls);
-        }
-        __syncthreads();
+    }
+    __syncthreads();
+    for (int i = tid; i < lanes.k; i += kThreads) {
+        if (lane_ids)
+            lane_ids[(int64_t)b * lanes.k + i] = li[i];
+        if (lane_max)
+            lane_max[(int64_t)b * lanes.k + i] = lv[i];
     }
     if (tid == 0) {
+        float rv = -INFINITY, rm = -INFINITY, rs = 0.f;
+        int ri = INT_MAX;
+        for (int i = 0; i < lanes.k; ++i) {
+            // a later lane wins only if strictly larger (its indices are higher)
+            if (better(lv[i], li[i], rv, ri)) {
+                rv = lv[i];
+                ri = li[i];
+            }
+            lse_merge(rm, rs, lm[i], ls[i]);
+        }
         ids[b] = ri;
-        const float l = rm + __logf(rs);
-        if (lse)
-            lse[b] = l;
-        if (sel_lp)
-            sel_lp[b] = rv - l;
+        if (mse) {
+            const float l = rm + __logf(rs);
+            if (lse)
+                lse[b] = l;
+            if (sel_lp)
+                sel_lp[b] = rv - l;
+        }
     }
 }
 
@@ -1121,18 +979,19 @@ __global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float *logit
 // One workgroup = 8 waves = a 256-row x 256-column block of one lane, laid
 // out as 4 (rows) x 2 (columns) waves; each wave owns 64 rows x one
 // 128-column tile, so the per-(row, tile) epilogue results come straight out
-// of one wave.  K advances in 32-row steps through a 3-stage LDS ring filled
-// by direct-to-LDS buffer loads (1 KB per instruction):
-//   * X stage [256 rows][32 k] bf16, 16-byte units XOR-swizzled by row so
+// of one wave.  K advances in 64-row stages through a 2-stage LDS ring filled
+// by direct-to-LDS buffer loads (1 KB per instruction), two 32-deep MFMA steps
+// per stage:
+//   * X stage [256 rows][64 k] bf16, 16-byte units XOR-swizzled by row so
 //     that the 16 lanes reading one k-group of 16 rows hit distinct banks;
-//   * W stage [32 k][256 columns] bf16, row-major as in HBM; a lane reads an
+//   * W stage [64 k][256 columns] bf16, row-major as in HBM; a lane reads an
 //     8 x 8 block (rows 8g..8g+7, columns 8n..8n+7) and transposes it in
 //     registers with v_perm, as in the decode kernel.
 // Each logit is accumulated over ascending K steps in one wave with
 // v_mfma_f32_16x16x32_bf16.  The token / log-prob / full-logit surfaces all
 // use this mainloop for large batches, so they stay bit-identical.
 // ---------------------------------------------------------------------------
-constexpr int kLBM = 256, kLBN = 256, kLBK = 64;
+constexpr int kLBM = kLargeRows, kLBN = 256, kLBK = kLargeStepK;
 constexpr int kLWaves = 8, kLThreads = kLWaves * 64;
 constexpr int kLStages = 2;                     // LDS ring depth (X and W stages)
 constexpr int kLStageXBytes = kLBM * kLBK * 2;  // 32 KB at BK = 64
@@ -1470,15 +1329,18 @@ hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
     const int rpg = kRowBlock * MB;
     const int ntiles = a.lanes.tile0[a.lanes.k];
     dim3 grid(((ntiles + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg) * a.kslices);
-    if constexpr (XP) {
-        const int nsteps = (a.H + kStepK - 1) / kStepK;
-        if (nsteps > 0) {
-            hipLaunchKernelGGL(pack_hidden_kernel<MB>, dim3(nsteps), dim3(MB * 64), 0, s, a.x,
-                               a.ldx, a.B, a.H, a.xp);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess)
-                return e;
-        }
+    const int nsteps = (a.H + kStepK - 1) / kStepK;
+    if (XP && nsteps > 0) {
+        // the pack launch also clears the call's counters and keys
+        hipLaunchKernelGGL(pack_hidden_kernel<MB>, dim3(nsteps), dim3(MB * 64), 0, s, a.x,
+                           a.ldx, a.B, a.H, a.xp, a.zero);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    } else {
+        const hipError_t e = launch_clear(a.zero, s);
+        if (e != hipSuccess)
+            return e;
     }
     switch (epi) {
     case kEpiPair:
@@ -1753,12 +1615,12 @@ hipError_t launch_head_gemm_large(const HeadArgs &a, int epi, hipStream_t s)
 
 hipError_t launch_combine(const int2 *pair, const float2 *mse, const LaneTable &lanes,
                           int32_t B, int32_t T, int32_t *ids, float *lse, float *sel_lp,
-                          hipStream_t s)
+                          int32_t *lane_ids, float *lane_max, hipStream_t s)
 {
     if (B <= 0)
         return hipSuccess;
     hipLaunchKernelGGL(combine_kernel, dim3(B), dim3(kThreads), 0, s, pair, mse, lanes, T, ids,
-                       lse, sel_lp);
+                       lse, sel_lp, lane_ids, lane_max);
     return hipGetLastError();
 }
 
@@ -1806,7 +1668,8 @@ hipError_t launch_row_argmax(const float *logits, int64_t ldl, int32_t B, int32_
     one.off[1] = V;
     one.tile0[0] = 0;
     one.tile0[1] = nchunks;
-    return launch_combine(partial, nullptr, one, B, nchunks, ids, nullptr, nullptr, s);
+    return launch_combine(partial, nullptr, one, B, nchunks, ids, nullptr, nullptr, nullptr,
+                          nullptr, s);
 }
 
 hipError_t launch_partial_gemm(const PartialArgs &a, hipStream_t s)

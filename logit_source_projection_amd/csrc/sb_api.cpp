@@ -18,25 +18,12 @@ constexpr size_t kRegionAlign = 256;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Every workspace starts with the same fixed region that must be zero on
-// entry and that every call leaves zero: completion counters (row groups x
-// lanes), per-lane keys (rows x lanes, for B <= 128) and per-tile slice
-// counters.  Its size does not depend on the call, so no call -- of any
-// shape, surface or entry point -- writes non-zero data where a later call
-// expects zeros.
-constexpr int kSmallGroups =
-    (sbk::kLargeBatch - 1 + sbk::kRowBlock * sbk::kMaxMB - 1) / (sbk::kRowBlock * sbk::kMaxMB);
-constexpr size_t kZeroSync = 0;
-constexpr size_t kZeroKeys =
-    (kZeroSync + kSmallGroups * (SB_MAX_LANES + 1) * sizeof(uint32_t) + kRegionAlign - 1) /
-    kRegionAlign * kRegionAlign;
-constexpr size_t kZeroSlices =
-    (kZeroKeys + (size_t)(sbk::kLargeBatch - 1) * SB_MAX_LANES * sizeof(uint64_t) +
-     kRegionAlign - 1) / kRegionAlign * kRegionAlign;
-constexpr size_t kZeroBytes =
-    (kZeroSlices + sbk::kMaxSplitTiles * sizeof(uint32_t) + kRegionAlign - 1) / kRegionAlign *
-    kRegionAlign;
-static_assert(kZeroBytes == 74496, "the size include/sb.h states for the zeroed region");
+// Every workspace starts with the same fixed region: the per-tile counters of
+// a head split into K slices.  A call on a split head clears the counters it
+// uses before its head kernel runs (a.zero), so the workspace's contents on
+// entry never matter.
+constexpr size_t kCtrBytes = sbk::kMaxSplitTiles * sizeof(uint32_t);
+static_assert(kCtrBytes == 8192, "the size include/sb.h states for the counter region");
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -78,9 +65,16 @@ sb_status check_desc(const sb_head_desc *d)
     if (d->B > kMaxRows)
         return SB_ERR_UNSUPPORTED;
     // Per-step buffer offsets are 32-bit: 40 hidden rows of a shard and one
-    // row group of x must span less than 4 GiB.
-    if ((int64_t)(sbk::kStepK + 8) * d->ldw * 2 >= ((int64_t)1 << 32) ||
-        (int64_t)(sbk::kRowBlock * sbk::kMaxMB) * d->ldx * 2 >= ((int64_t)1 << 32))
+    // row group of x must span less than 4 GiB; for the large-batch kernel
+    // (B >= 129) a K stage of a shard (64 rows, plus 8) and a 256-row block
+    // of x.
+    const int64_t lim = (int64_t)1 << 32;
+    if ((int64_t)(sbk::kStepK + 8) * d->ldw * 2 >= lim ||
+        (int64_t)(sbk::kRowBlock * sbk::kMaxMB) * d->ldx * 2 >= lim)
+        return SB_ERR_UNSUPPORTED;
+    if (d->B >= sbk::kLargeBatch &&
+        ((int64_t)(sbk::kLargeStepK + 8) * d->ldw * 2 >= lim ||
+         (int64_t)sbk::kLargeRows * d->ldx * 2 >= lim))
         return SB_ERR_UNSUPPORTED;
     return SB_OK;
 }
@@ -92,9 +86,8 @@ int shard_ld(int vi) { return (vi + 3) & ~3; }
 struct Layout {
     int T = 0;            // tile capacity: row stride of the (row, tile) regions
     int nchunks = 0;      // full-logit argmax chunks per row
-    int groups = 0;       // row groups (grid y) of the head GEMM
     int kslices = 1;      // K slices of the head GEMM (one row group only)
-    size_t sync = 0, keys = 0, kctr = 0, kpart = 0, xp = 0, pair = 0, mse = 0, lane_mse = 0;
+    size_t kctr = 0, kpart = 0, xp = 0, pair = 0, mse = 0;
     size_t shard[SB_MAX_LANES] = {}, partial = 0;
     size_t total = 0;
 };
@@ -112,13 +105,9 @@ Layout layout(const sb_head_desc *d, int surface)
     if (B == 0)
         return L;
     const int rpg = sbk::rows_per_group(d->B);
-    L.groups = (d->B + rpg - 1) / rpg;
-    const bool large = d->B >= sbk::kLargeBatch;
     const bool lse = surface == SB_SURF_LOGPROBS || surface == SB_SURF_LOGPROBS_FULL;
-    L.sync = kZeroSync;
-    L.keys = kZeroKeys;
-    L.kctr = kZeroSlices;
-    at = kZeroBytes;
+    L.kctr = 0;
+    at = kCtrBytes;
     L.kslices = sbk::k_slices(d->B, d->H, d->V);
     if (L.kslices > 1) {
         // partial tiles of the K slices, [T][kslices][rows per group][kTileN]
@@ -135,22 +124,12 @@ Layout layout(const sb_head_desc *d, int surface)
     case SB_SURF_TOKENS:
     case SB_SURF_LOGPROBS:
     case SB_SURF_LOGPROBS_FULL:
-        if (large) {
-            // large-batch kernel: (row, tile) results, folded by the combine kernel
-            L.pair = at;
-            at = align_up(at + B * L.T * sizeof(int2), kRegionAlign);
-            if (lse) {
-                L.mse = at;
-                at = align_up(at + B * L.T * sizeof(float2), kRegionAlign);
-            }
-            break;
-        }
-        // completion counters and lane keys: in the zeroed region
+        // (row, tile) results, folded by the combine launch
+        L.pair = at;
+        at = align_up(at + B * L.T * sizeof(int2), kRegionAlign);
         if (lse) {
             L.mse = at;
             at = align_up(at + B * L.T * sizeof(float2), kRegionAlign);
-            L.lane_mse = at;
-            at = align_up(at + B * d->k * sizeof(float2), kRegionAlign);
         }
         break;
     case SB_SURF_FULL_LOGITS:
@@ -210,17 +189,22 @@ void fill_args(const sb_head_desc *d, const Layout &L, sbk::HeadArgs &a)
     a.mse = nullptr;
     a.out = nullptr;
     a.ldo = 0;
-    a.sync = nullptr;
-    a.keys = nullptr;
-    a.lane_mse = nullptr;
-    a.ids = nullptr;
-    a.lse = nullptr;
-    a.sel_lp = nullptr;
     a.kslices = L.kslices;
     a.slice_steps = sbk::slice_steps(d->H, L.kslices);
     a.kpart = nullptr;
     a.kctr = nullptr;
     a.xp = nullptr;
+    memset(&a.zero, 0, sizeof a.zero);
+}
+
+// The words the head launch needs at zero: the slice counters of a split
+// head.  Call after the regions are set.
+void set_zero(sbk::HeadArgs &a)
+{
+    if (a.kctr) {
+        a.zero.p[0] = a.kctr;
+        a.zero.n[0] = a.lanes.tile0[a.lanes.k];
+    }
 }
 
 // The K-slice regions of a split head and the packed hidden rows of 33-64
@@ -248,6 +232,35 @@ sb_status check_ws(const Layout &L, void *ws, size_t ws_bytes)
     return SB_OK;
 }
 
+
+// Token surface, optionally with the per-lane results.
+sb_status project_tokens(const sb_head_desc *desc, int32_t *ids, int32_t *lane_ids,
+                         float *lane_max, void *ws, size_t ws_bytes, void *stream)
+{
+    sb_status st = check_desc(desc);
+    if (st != SB_OK)
+        return st;
+    if (desc->B == 0)
+        return SB_OK;
+    if (!ids)
+        return SB_ERR_NULL;
+    const Layout L = layout(desc, SB_SURF_TOKENS);
+    if ((st = check_ws(L, ws, ws_bytes)) != SB_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    sbk::HeadArgs a;
+    fill_args(desc, L, a);
+    a.pair = region<int2>(ws, L.pair);
+    set_slices(L, ws, a);
+    set_zero(a);
+    const hipError_t e = a.B >= sbk::kLargeBatch ? sbk::launch_head_gemm_large(a, sbk::kEpiPair, s)
+                                                  : sbk::launch_head_gemm(a, sbk::kEpiPair, s);
+    if (e != hipSuccess ||
+        sbk::launch_combine(a.pair, nullptr, a.lanes, a.B, a.T, ids, nullptr, nullptr, lane_ids,
+                            lane_max, s) != hipSuccess)
+        return SB_ERR_HIP;
+    return SB_OK;
+}
 
 // ---------------------------------------------------------------------------
 // Partial completion
@@ -299,13 +312,13 @@ int partial_chunks(const sb_partial_desc *d)
     return n;
 }
 
-// The chunk partials sit after the head calls' zeroed region, so that one
+// The chunk partials sit after the head calls' counter region, so that one
 // workspace can serve both kinds of call.
 size_t partial_bytes(const sb_partial_desc *d)
 {
     if (d->B == 0)
         return 0;  // nothing is read or written
-    return kZeroBytes + align_up((size_t)partial_chunks(d) * (size_t)d->B *
+    return kCtrBytes + align_up((size_t)partial_chunks(d) * (size_t)d->B *
                                      (size_t)shard_ld(d->N) * sizeof(float),
                                  kRegionAlign);
 }
@@ -329,34 +342,13 @@ size_t sb_workspace_bytes(const sb_head_desc *desc, int surface, sb_status *stat
 sb_status sb_project_tokens(const sb_head_desc *desc, int32_t *ids, void *ws, size_t ws_bytes,
                             void *stream)
 {
-    sb_status st = check_desc(desc);
-    if (st != SB_OK)
-        return st;
-    if (desc->B == 0)
-        return SB_OK;
-    if (!ids)
-        return SB_ERR_NULL;
-    const Layout L = layout(desc, SB_SURF_TOKENS);
-    if ((st = check_ws(L, ws, ws_bytes)) != SB_OK)
-        return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    sbk::HeadArgs a;
-    fill_args(desc, L, a);
-    a.ids = ids;
-    if (a.B >= sbk::kLargeBatch) {
-        a.pair = region<int2>(ws, L.pair);
-        if (sbk::launch_head_gemm_large(a, sbk::kEpiPair, s) != hipSuccess ||
-            sbk::launch_combine(a.pair, nullptr, a.lanes, a.B, a.T, ids, nullptr, nullptr, s) !=
-                hipSuccess)
-            return SB_ERR_HIP;
-        return SB_OK;
-    }
-    a.sync = region<uint32_t>(ws, L.sync);
-    a.keys = region<unsigned long long>(ws, L.keys);
-    set_slices(L, ws, a);
-    if (sbk::launch_head_gemm(a, sbk::kEpiPair, s) != hipSuccess)
-        return SB_ERR_HIP;
-    return SB_OK;
+    return project_tokens(desc, ids, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+sb_status sb_project_lane_results(const sb_head_desc *desc, int32_t *ids, int32_t *lane_ids,
+                                  float *lane_max, void *ws, size_t ws_bytes, void *stream)
+{
+    return project_tokens(desc, ids, lane_ids, lane_max, ws, ws_bytes, stream);
 }
 
 sb_status sb_project_logprobs(const sb_head_desc *desc, int32_t *ids, float *lse, float *sel_lp,
@@ -382,29 +374,19 @@ sb_status sb_project_logprobs(const sb_head_desc *desc, int32_t *ids, float *lse
     hipStream_t s = static_cast<hipStream_t>(stream);
     sbk::HeadArgs a;
     fill_args(desc, L, a);
+    a.pair = region<int2>(ws, L.pair);
     a.mse = region<float2>(ws, L.mse);
-    if (a.B >= sbk::kLargeBatch) {
-        a.pair = region<int2>(ws, L.pair);
-    } else {
-        a.sync = region<uint32_t>(ws, L.sync);
-        a.keys = region<unsigned long long>(ws, L.keys);
-        a.lane_mse = region<float2>(ws, L.lane_mse);
-        set_slices(L, ws, a);
-    }
-    a.ids = ids;
-    a.lse = lse;
-    a.sel_lp = sel_lp;
+    set_slices(L, ws, a);
+    set_zero(a);
     a.out = logprobs;
     a.ldo = ldlp;
     const int epi = logprobs ? sbk::kEpiPairLseOut : sbk::kEpiPairLse;
-    if (a.B >= sbk::kLargeBatch) {
-        if (sbk::launch_head_gemm_large(a, epi, s) != hipSuccess ||
-            sbk::launch_combine(a.pair, a.mse, a.lanes, a.B, a.T, ids, lse, sel_lp, s) !=
-                hipSuccess)
-            return SB_ERR_HIP;
-    } else if (sbk::launch_head_gemm(a, epi, s) != hipSuccess) {
+    const hipError_t e = a.B >= sbk::kLargeBatch ? sbk::launch_head_gemm_large(a, epi, s)
+                                                  : sbk::launch_head_gemm(a, epi, s);
+    if (e != hipSuccess ||
+        sbk::launch_combine(a.pair, a.mse, a.lanes, a.B, a.T, ids, lse, sel_lp, nullptr, nullptr,
+                            s) != hipSuccess)
         return SB_ERR_HIP;
-    }
     if (logprobs && sbk::launch_normalize(logprobs, ldlp, lse, a.B, a.V, s) != hipSuccess)
         return SB_ERR_HIP;
     return SB_OK;
@@ -435,6 +417,7 @@ sb_status sb_full_logits(const sb_head_desc *desc, float *logits, int64_t ldl, i
         a.lanes.shard_ld[i] = shard_ld(lane_width(desc, i));
     }
     set_slices(L, ws, a);
+    set_zero(a);
     const hipError_t e = a.B >= sbk::kLargeBatch ? sbk::launch_head_gemm_large(a, sbk::kEpiShard, s)
                                                   : sbk::launch_head_gemm(a, sbk::kEpiShard, s);
     if (e != hipSuccess)
@@ -495,7 +478,7 @@ sb_status sb_partial_complete(const sb_partial_desc *desc, int op, float *out, i
     a.B = desc->B;
     a.N = desc->N;
     a.T = (desc->N + sbk::kTileN - 1) / sbk::kTileN;
-    a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + kZeroBytes);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + kCtrBytes);
     a.ldp = shard_ld(desc->N);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (sbk::launch_partial_gemm(a, s) != hipSuccess ||

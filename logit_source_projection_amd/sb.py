@@ -3,7 +3,8 @@
 Every step of the head runs in libsb's HIP kernels.  PyTorch provides device
 memory and the stream; this module builds the C descriptor from tensors,
 allocates the workspace through torch when none is given, and raises
-``SbError`` on a non-zero status.  There is no fallback: if libsb.so is
+``SbError`` on a non-zero status.  A workspace allocated here is allocated on
+the call's stream and recorded as used by it.  There is no fallback: if libsb.so is
 missing, loading fails with an error.
 """
 import ctypes
@@ -36,9 +37,9 @@ SB_RED_MIN = 2
 SB_RED_MAX = 3
 REDUCE_OPS = {"sum": SB_RED_SUM, "prod": SB_RED_PROD, "min": SB_RED_MIN, "max": SB_RED_MAX}
 
-EXPORTS = ("sb_workspace_bytes", "sb_project_tokens", "sb_project_logprobs",
-           "sb_full_logits", "sb_partial_workspace_bytes", "sb_partial_complete",
-           "sb_status_string")
+EXPORTS = ("sb_workspace_bytes", "sb_project_tokens", "sb_project_lane_results",
+           "sb_project_logprobs", "sb_full_logits", "sb_partial_workspace_bytes",
+           "sb_partial_complete", "sb_status_string")
 
 
 class SbError(RuntimeError):
@@ -85,6 +86,8 @@ def lib():
     L.sb_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     L.sb_project_tokens.restype = ctypes.c_int
     L.sb_project_tokens.argtypes = [P, vp, vp, sz, vp]
+    L.sb_project_lane_results.restype = ctypes.c_int
+    L.sb_project_lane_results.argtypes = [P, vp, vp, vp, vp, sz, vp]
     L.sb_project_logprobs.restype = ctypes.c_int
     L.sb_project_logprobs.argtypes = [P, vp, vp, vp, vp, i64, vp, sz, vp]
     L.sb_full_logits.restype = ctypes.c_int
@@ -176,16 +179,31 @@ def sb_workspace_bytes(head, surface):
 
 
 def workspace(head, surface, device="cuda"):
-    """A zero-filled workspace for `surface` (the ABI requires a zeroed
-    workspace on first use; every call leaves it reusable)."""
+    """A workspace for `surface` (its contents on entry do not matter: every
+    call clears what it relies on)."""
     n = sb_workspace_bytes(head, surface)
-    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
-def _workspace(head, surface, ws, device):
+def _workspace(nbytes_fn, ws, device, stream):
+    """The caller's workspace, or a temporary one allocated on the call's
+    stream and marked as used by it, so that the caching allocator does not
+    hand its memory to other work before the call's kernels are done."""
     if ws is not None:
         return ws
-    return workspace(head, surface, device)
+    s = _torch_stream(stream, device)
+    with torch.cuda.stream(s):
+        t = torch.empty(max(nbytes_fn(), 16), dtype=torch.uint8, device=device)
+    t.record_stream(s)
+    return t
+
+
+def _torch_stream(stream, device):
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
 
 
 def _check(status, where):
@@ -195,9 +213,19 @@ def _check(status, where):
 
 def sb_project_tokens(head, ids, ws=None, stream=None):
     """Token-only surface: ids (int32 [B], device) <- argmax token IDs."""
-    ws = _workspace(head, SB_SURF_TOKENS, ws, ids.device)
+    ws = _workspace(lambda: sb_workspace_bytes(head, SB_SURF_TOKENS), ws, ids.device, stream)
     _check(lib().sb_project_tokens(head.ref(), _ptr(ids), _ptr(ws), ws.numel(),
                                    _stream(stream)), "sb_project_tokens")
+    return ids
+
+
+def sb_project_lane_results(head, ids, lane_ids=None, lane_max=None, ws=None, stream=None):
+    """Token surface plus each lane's own result: lane_ids (int32 [B, k]) and
+    lane_max (fp32 [B, k]) of every row, either optional."""
+    ws = _workspace(lambda: sb_workspace_bytes(head, SB_SURF_TOKENS), ws, ids.device, stream)
+    _check(lib().sb_project_lane_results(head.ref(), _ptr(ids), _ptr(lane_ids), _ptr(lane_max),
+                                         _ptr(ws), ws.numel(), _stream(stream)),
+           "sb_project_lane_results")
     return ids
 
 
@@ -206,7 +234,7 @@ def sb_project_logprobs(head, ids, lse, sel_lp=None, logprobs=None, ws=None,
     """Log-probability surface: ids, lse, optional sel_lp and complete
     fp32 log-probs [B, V] (row stride logprobs.stride(0))."""
     surf = SB_SURF_LOGPROBS_FULL if logprobs is not None else SB_SURF_LOGPROBS
-    ws = _workspace(head, surf, ws, ids.device)
+    ws = _workspace(lambda: sb_workspace_bytes(head, surf), ws, ids.device, stream)
     ld = logprobs.stride(0) if logprobs is not None else 0
     _check(lib().sb_project_logprobs(head.ref(), _ptr(ids), _ptr(lse), _ptr(sel_lp),
                                      _ptr(logprobs), ld, _ptr(ws), ws.numel(),
@@ -217,7 +245,8 @@ def sb_project_logprobs(head, ids, lse, sel_lp=None, logprobs=None, ws=None,
 def sb_full_logits(head, logits, ids=None, ws=None, stream=None):
     """Full-logit plan: logits fp32 [B, V] (row stride logits.stride(0)),
     optional ids."""
-    ws = _workspace(head, SB_SURF_FULL_LOGITS, ws, logits.device)
+    ws = _workspace(lambda: sb_workspace_bytes(head, SB_SURF_FULL_LOGITS), ws, logits.device,
+                    stream)
     _check(lib().sb_full_logits(head.ref(), _ptr(logits), logits.stride(0), _ptr(ids),
                                 _ptr(ws), ws.numel(), _stream(stream)), "sb_full_logits")
     return logits
@@ -277,9 +306,7 @@ def sb_partial_complete(part, op, out, ws=None, stream=None):
     reduction `op` ("sum", "prod", "min", "max" or an SB_RED_* code) of the
     lane partials."""
     code = REDUCE_OPS[op] if isinstance(op, str) else int(op)
-    if ws is None:
-        ws = torch.empty(max(sb_partial_workspace_bytes(part), 16), dtype=torch.uint8,
-                         device=out.device)
+    ws = _workspace(lambda: sb_partial_workspace_bytes(part), ws, out.device, stream)
     _check(lib().sb_partial_complete(part.ref(), code, _ptr(out), out.stride(0), _ptr(ws),
                                      ws.numel(), _stream(stream)), "sb_partial_complete")
     return out

@@ -8,18 +8,18 @@ it; the product path never calls it.
 Sources (SemBridge: Compiling Consumer Observations into Cross-Stack
 Communication Plans):
 
-* section 5.2 (Data, Result, and Control Paths): the tail output head
-  materialises the full logits; the full-logit plan slices them by TP lane,
-  transfers the shards and reconstructs the whole tensor with a
-  destination-local AllGather, while a token-only request applies the native
-  (deterministic) sampler to the same tensor and ships int32 IDs;
-* section 5.3 / section 6 (Plan Realization, Evaluation): source projection
-  applies the same argmax before transfer and sends one int32 result per lane;
-* section 3.1 (Boundary Contract): the registered projection operator carries
-  deterministic tie-breaking semantics; section 3.2 (Consumer Observation):
-  a log-probability surface keeps the complete logits plus token IDs;
-* Figure 1 caption: full-logit transfer and source projection deliver the
-  same requested token ID.
+* section 5.2 (Data, Result, and Control Paths): the output head produces
+  the logits; the full-logit plan cuts them into per-lane shards, moves the
+  shards and rebuilds the whole tensor at the destination, whereas the
+  token-only plan runs the deterministic sampler on the same logits at the
+  source and moves int32 token IDs only;
+* section 5.3 / section 6 (Plan Realization, Evaluation): under source
+  projection each lane runs the argmax before the transfer, so a lane
+  contributes one int32 result per row;
+* section 3.1 (Boundary Contract): a projection operator must declare how it
+  breaks ties, deterministically; section 3.2 (Consumer Observation): a
+  log-probability consumer needs the complete logits as well as the IDs;
+* Figure 1 caption: both plans hand the consumer the same token ID.
 
 Readings taken where the pages are silent:
 

@@ -5,15 +5,15 @@
 What it computes (SemBridge paper, "SemBridge: Compiling Consumer Observations
 into Cross-Stack Communication Plans"):
 
-* section 6.4 (Exact Shards and Partial Completion): the MLP down projection
-  is row parallel -- lane i holds a distinct activation shard X_i [B, K_i] and
-  the matching rows W_i [K_i, N] of the weight, and produces an incomplete
-  full-width partial P_i = X_i . W_i that must be reduced before a complete
-  downstream observation;
-* section 3.6 (Contract Construction and Static Validation): a reduction
-  obligation names an elementwise operator over a source set -- the
-  executable reference supports sum, product, minimum and maximum -- and
-  lowering completes the registered operator before exposing a full value.
+* section 6.4 (Exact Shards and Partial Completion): in the MLP down
+  projection each lane multiplies its own slice of the intermediate
+  activations by its own rows of the weight, so every lane ends up with a
+  full-width but incomplete result P_i = X_i . W_i that is not an observable
+  value on its own;
+* section 3.6 (Contract Construction and Static Validation): the contract
+  carries an elementwise operator (sum, product, minimum or maximum in the
+  paper's reference) that the plan must apply to all the partials before
+  any consumer sees the output.
 
 Reading taken where the pages are silent: the k partials are folded in
 ascending lane order, out = op(...op(op(P_0, P_1), P_2)..., P_{k-1}).  Every

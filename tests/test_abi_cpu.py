@@ -74,26 +74,37 @@ def up256(n):
     return (n + 255) // 256 * 256
 
 
-# Every workspace starts with one fixed zeroed region, whatever the call:
-# completion counters for up to 2 row groups x 65, per-lane keys for up to
-# 128 rows x 64 lanes (8 B each), then 2048 per-tile slice counters.
-ZERO = up256(up256(up256(2 * 65 * 4) + 128 * 64 * 8) + 2048 * 4)
+# Every workspace starts with one fixed region, whatever the call: 2048
+# per-tile slice counters (u32) of a head split into K slices.
+ZERO = 2048 * 4
+
+
+def cap(off):
+    """Tile capacity: per lane ceil((V_i + 56) / 128), room for a lane grid
+    shifted by up to 56 columns onto a cache-line boundary."""
+    return sum((off[i + 1] - off[i] + 56 + 127) // 128 for i in range(len(off) - 1))
+
+
+def pairs(B, off):
+    """The (row, tile) results the combine launch folds: 8 B per (row, tile)."""
+    return up256(B * cap(off) * 8)
 
 
 def test_workspace_bytes_for_the_workloads():
-    assert ZERO == 74496
-    h = fake_head(B=16, H=5120, V=151936, off=(0, 37984, 75968, 113952, 151936))
-    # tile capacity per lane: ceil((37984 + 56) / 128), room for a lane grid
-    # shifted by up to 56 columns onto a cache-line boundary
-    T = 4 * 298
-    # the dense head has enough tiles (1187) for one workgroup each: no slices
-    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == ZERO
-    # + per-tile (max, sum-exp) pairs and per-lane pairs
+    assert ZERO == 8192
+    off = (0, 37984, 75968, 113952, 151936)
+    h = fake_head(B=16, H=5120, V=151936, off=off)
+    assert cap(off) == 4 * 298
+    # the dense head has enough tiles (1187) for one workgroup each: no
+    # slices; the (max, lowest index) pair of every (row, tile)
+    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == ZERO + pairs(16, off)
+    # + the (tile max, sum-exp) pairs
     lp = sb.sb_workspace_bytes(h, sb.SB_SURF_LOGPROBS)
-    assert lp == ZERO + 16 * T * 8 + 512
-    # large batches: per-tile pairs for the combine kernel only
-    hl = fake_head(B=300, H=5120, V=151936, off=(0, 37984, 75968, 113952, 151936))
-    assert sb.sb_workspace_bytes(hl, sb.SB_SURF_TOKENS) == ZERO + up256(300 * T * 8)
+    assert lp == ZERO + 2 * pairs(16, off)
+    assert sb.sb_workspace_bytes(h, sb.SB_SURF_LOGPROBS_FULL) == lp
+    # large batches: the same regions
+    hl = fake_head(B=300, H=5120, V=151936, off=off)
+    assert sb.sb_workspace_bytes(hl, sb.SB_SURF_TOKENS) == ZERO + pairs(300, off)
     full = sb.sb_workspace_bytes(h, sb.SB_SURF_FULL_LOGITS)
     assert full >= ZERO + 16 * 151936 * 4
     assert sb.sb_workspace_bytes(fake_head(B=0), sb.SB_SURF_TOKENS) == 0
@@ -103,31 +114,40 @@ def test_workspace_bytes_of_a_split_head():
     # A head of 64 tiles (V = 8192) splits its 160 hidden steps into 4 slices
     # of 40, and each slice writes a 16 x 128 fp32 partial tile per tile of
     # the capacity (65 tiles, with room for a lane grid shifted by 56 columns).
-    h = fake_head(B=16, H=5120, V=8192, off=(0, 8192))
-    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == ZERO + 65 * 4 * 16 * 128 * 4
+    off = (0, 8192)
+    h = fake_head(B=16, H=5120, V=8192, off=off)
+    assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == \
+        ZERO + 65 * 4 * 16 * 128 * 4 + pairs(16, off)
     # the split depends on (B, H, V), not on the lane split
-    h4 = fake_head(B=16, H=5120, V=8192, off=(0, 2048, 4096, 6144, 8192))
-    assert sb.sb_workspace_bytes(h4, sb.SB_SURF_TOKENS) == ZERO + 4 * 17 * 4 * 16 * 128 * 4
+    off4 = (0, 2048, 4096, 6144, 8192)
+    h4 = fake_head(B=16, H=5120, V=8192, off=off4)
+    assert sb.sb_workspace_bytes(h4, sb.SB_SURF_TOKENS) == \
+        ZERO + 4 * 17 * 4 * 16 * 128 * 4 + pairs(16, off4)
     # 127 tiles: 3 slices (of 56, 56 and 48 steps); 64 rows: 64-row partial tiles,
     # then the hidden rows packed per 32-deep step (4 row blocks x 64 lanes x 16 B)
-    h = fake_head(B=64, H=5120, V=16256, off=(0, 16256))
+    off = (0, 16256)
+    h = fake_head(B=64, H=5120, V=16256, off=off)
     assert sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS) == \
-        ZERO + 128 * 3 * 64 * 128 * 4 + 160 * 4096
+        ZERO + 128 * 3 * 64 * 128 * 4 + 160 * 4096 + pairs(64, off)
     # one GPU's lane of the dense head (297 tiles, just past one tile per CU,
     # 16 rows): 2 slices of 80 steps, partial tiles for the 298 tiles of capacity
-    assert sb.sb_workspace_bytes(fake_head(B=16, H=5120, V=37984, off=(0, 37984)),
-                                 sb.SB_SURF_TOKENS) == ZERO + 298 * 2 * 16 * 128 * 4
+    off = (0, 37984)
+    assert sb.sb_workspace_bytes(fake_head(B=16, H=5120, V=37984, off=off),
+                                 sb.SB_SURF_TOKENS) == ZERO + 298 * 2 * 16 * 128 * 4 + pairs(16, off)
     # ... but not at 17 rows, at H = 2048 (64 steps), at 256 or at 353 tiles
     for kw in (dict(B=17, H=5120, V=37984), dict(B=16, H=2048, V=37984),
                dict(B=16, H=5120, V=256 * 128), dict(B=16, H=5120, V=353 * 128)):
-        assert sb.sb_workspace_bytes(fake_head(off=(0, kw["V"]), **kw),
-                                     sb.SB_SURF_TOKENS) == ZERO, kw
+        off = (0, kw["V"])
+        assert sb.sb_workspace_bytes(fake_head(off=off, **kw),
+                                     sb.SB_SURF_TOKENS) == ZERO + pairs(kw["B"], off), kw
     # one GPU's lane of the MoE head (594 tiles): the packed hidden rows only
-    assert sb.sb_workspace_bytes(fake_head(B=64, H=4096, V=75968, off=(0, 75968)),
-                                 sb.SB_SURF_TOKENS) == ZERO + 128 * 4096
+    off = (0, 75968)
+    assert sb.sb_workspace_bytes(fake_head(B=64, H=4096, V=75968, off=off),
+                                 sb.SB_SURF_TOKENS) == ZERO + 128 * 4096 + pairs(64, off)
     # fewer than 32 hidden steps (H <= 992): never split
-    assert sb.sb_workspace_bytes(fake_head(B=16, H=992, V=1024, off=(0, 1024)),
-                                 sb.SB_SURF_TOKENS) == ZERO
+    off = (0, 1024)
+    assert sb.sb_workspace_bytes(fake_head(B=16, H=992, V=1024, off=off),
+                                 sb.SB_SURF_TOKENS) == ZERO + pairs(16, off)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -155,6 +175,40 @@ def test_descriptor_validation(kw, status):
     h = fake_head(**kw)
     assert ws_status(h) == status
     assert tokens_status(h) == status
+
+
+def test_large_batch_offset_limits():
+    """From 129 rows the large-batch kernel's 32-bit buffer offsets span a
+    256-row block of x and a 64-row K stage of a shard (plus 8 rows of
+    slack): validation rejects strides where those reach 4 GiB, and accepts
+    them below 129 rows, where the decode kernels reach 64 rows of x and 40
+    rows of a shard."""
+    ldx = 1 << 23                   # 256 rows x 2 B = 4 GiB
+    ldw = 29826168                  # 72 rows x 2 B >= 4 GiB > 40 rows x 2 B
+    assert (256 * ldx * 2 >= 1 << 32) and (72 * ldw * 2 >= 1 << 32) and (40 * ldw * 2 < 1 << 32)
+    assert ws_status(fake_head(B=129, ldx=ldx)) == sb.SB_ERR_UNSUPPORTED
+    assert ws_status(fake_head(B=128, ldx=ldx)) == sb.SB_OK
+    assert ws_status(fake_head(B=129, ldx=ldx - 8)) == sb.SB_OK
+    assert ws_status(fake_head(B=129, ldw=ldw)) == sb.SB_ERR_UNSUPPORTED
+    assert ws_status(fake_head(B=128, ldw=ldw)) == sb.SB_OK
+    assert ws_status(fake_head(B=2048, ldw=ldw - 8)) == sb.SB_OK
+    assert tokens_status(fake_head(B=129, ldx=ldx)) == sb.SB_ERR_UNSUPPORTED
+    assert tokens_status(fake_head(B=300, ldw=ldw)) == sb.SB_ERR_UNSUPPORTED
+
+
+def test_lane_results_checks():
+    h = fake_head()
+    L = sb.lib()
+    need = sb.sb_workspace_bytes(h, sb.SB_SURF_TOKENS)
+    # ids are required, the per-lane outputs are optional; the token
+    # surface's workspace size applies
+    assert L.sb_project_lane_results(h.ref(), None, FAKE, FAKE, FAKE, need, None) == sb.SB_ERR_NULL
+    assert L.sb_project_lane_results(h.ref(), FAKE, None, None, FAKE, need - 1,
+                                     None) == sb.SB_ERR_WORKSPACE
+    assert L.sb_project_lane_results(fake_head(B=-1).ref(), FAKE, FAKE, FAKE, FAKE, need,
+                                     None) == sb.SB_ERR_SHAPE
+    assert L.sb_project_lane_results(fake_head(B=0, x_ptr=0).ref(), None, None, None, None, 0,
+                                     None) == sb.SB_OK
 
 
 def test_too_many_lanes():
@@ -222,7 +276,7 @@ def partial_status(p, op=sb.SB_RED_SUM, out=FAKE, ldo=None, ws=FAKE, ws_bytes=1 
 
 def test_partial_workspace_bytes():
     # two lanes of 8704 rows -> 9 + 9 chunks of 1024 rows, fp32 [B][N] each
-    # (after the head calls' zeroed region, so that one workspace serves both)
+    # (after the head calls' counter region, so that one workspace serves both)
     p = fake_partial()
     assert sb.sb_partial_workspace_bytes(p) == ZERO + 18 * 16 * 5120 * 4
     # ragged: 1000 + 1025 rows -> 1 + 2 chunks; N = 130 -> row stride 132

@@ -1,0 +1,102 @@
+"""GPU parity of each lane's own result (SemBridge Figure 1 caption and
+section 5.2: under source projection every lane ships one int32 result per
+row), through sb_project_lane_results.
+
+Checked element by element:
+  * against the oracle's per-lane argmax (lane_arg) and maximum (lane_max):
+    lane IDs equal on every (row, lane) whose top-2 gap inside the lane is
+    >= 2e-3 * max_v |z[row]| (the same near-tie rule as the row IDs, applied
+    to the lane's columns; the exempt pairs come from a full sort of the
+    lane's logits); lane maxima within the logit tolerance;
+  * against the GPU's own full logits (sb_full_logits), bit for bit: the lane
+    ID is the lowest index of the lane's largest fp32 logit and the lane
+    maximum is that logit;
+  * the row ID is the lane ID of the first lane whose maximum is largest.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from logit_source_projection_amd import inputs, sb
+from tests.gpu_common import LOGIT_REL, upload
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, H, V, lane offsets, separate lane allocations
+    (4, 256, 4096, [0, 2048, 4096], False),
+    (3, 200, 1000, [0, 1, 129, 130, 999, 1000], True),     # one-column lanes
+    (16, 512, 8192, list(range(0, 8193, 128)), True),       # 64 lanes (maximum)
+    (20, 640, 9001, [0, 3000, 3001, 9001], True),          # two row blocks, ragged
+    (48, 1024, 30000, inputs.equal_lanes(30000, 7), True),  # packed hidden rows
+    (16, 4160, 37984, [0, 37984], False),                   # two K slices
+    (100, 512, 20000, [0, 7, 19000, 20000], True),          # two-tile kernel
+    (300, 136, 6000, [0, 2500, 2501, 6000], True),          # large-batch kernel
+    (129, 64, 2050, inputs.equal_lanes(2050, 50), True),    # large-batch, 50 lanes
+]
+
+
+def lane_near_ties(z, off):
+    """[B, k] flags: the lane's top-2 gap (from a full sort of the lane's
+    logits) is below 2e-3 * max |z[row]|; one-column lanes have none."""
+    B, k = z.shape[0], len(off) - 1
+    scale = np.abs(z).max(axis=1)
+    out = np.zeros((B, k), dtype=bool)
+    for i in range(k):
+        seg = np.sort(z[:, off[i]:off[i + 1]], axis=1)
+        if seg.shape[1] > 1:
+            out[:, i] = seg[:, -1] - seg[:, -2] < 2e-3 * scale
+    return out
+
+
+@pytest.mark.parametrize("B,H,V,off,sep", CASES)
+def test_lane_results(require_gpu, B, H, V, off, sep):
+    print(f"lane results B={B} H={H} V={V} k={len(off) - 1}", flush=True)
+    d = inputs.make_random(B, H, V, off, seed=B * 7 + len(off))
+    widths = np.diff(off)
+    wide = int(np.argmax(widths))  # a lane of at least two columns
+    tie_a, tie_b = off[wide] + 1, off[wide + 1] - 2
+    if B >= 3:
+        # row 1: an exact tie between the last columns of the first and last
+        # lanes; row 2: one inside the widest lane
+        inputs.plant_equal_columns(d["x"], d["w"], 1, (off[1] - 1, off[-1] - 1), 40.0)
+        inputs.plant_equal_columns(d["x"], d["w"], 2, (tie_a, tie_b), 40.0)
+    head = upload(d, lanes_separate=sep)
+    k = len(off) - 1
+    ids = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    ids_tok = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    lane_ids = torch.full((B, k), -1, dtype=torch.int32, device="cuda")
+    lane_max = torch.full((B, k), float("nan"), dtype=torch.float32, device="cuda")
+    ldv = (V + 3) // 4 * 4
+    logits = torch.empty((B, ldv), dtype=torch.float32, device="cuda")[:, :V]
+    sb.sb_project_lane_results(head, ids, lane_ids, lane_max)
+    sb.sb_project_tokens(head, ids_tok)
+    sb.sb_full_logits(head, logits)
+    torch.cuda.synchronize()
+    ids, ids_tok = ids.cpu().numpy(), ids_tok.cpu().numpy()
+    li, lm, lg = lane_ids.cpu().numpy(), lane_max.cpu().numpy(), logits.cpu().numpy()
+
+    # the GPU's own logits, bit for bit
+    assert np.array_equal(ids, ids_tok)
+    for i in range(k):
+        seg = lg[:, off[i]:off[i + 1]]
+        assert np.array_equal(li[:, i], off[i] + np.argmax(seg, axis=1)), i
+        assert np.array_equal(lm[:, i], seg.max(axis=1)), i
+    first_best = np.argmax(lm == lm.max(axis=1, keepdims=True), axis=1)
+    assert np.array_equal(ids, li[np.arange(B), first_best])
+
+    # the oracle's per-lane results
+    z = oracle.logits(d["x"], d["w"])
+    r = oracle.project(z, off)
+    near = lane_near_ties(z, off)
+    bad = (li != r["lane_arg"]) & ~near
+    assert not bad.any(), f"lane id mismatch at {np.argwhere(bad)[:5].tolist()}"
+    scale = np.abs(z).max(axis=1, keepdims=True)
+    assert np.all(np.abs(lm.astype(np.float64) - r["lane_max"]) <= LOGIT_REL * scale)
+    if B >= 3:
+        # planted exact ties: both lanes report their own column, and the row
+        # goes to the lower one
+        assert li[1, 0] == off[1] - 1 and li[1, k - 1] == off[-1] - 1 and ids[1] == off[1] - 1
+        assert li[2, wide] == tie_a and ids[2] == tie_a
+    print(f"  exempt (row, lane) pairs: {int(near.sum())} of {near.size}", flush=True)

@@ -21,21 +21,23 @@ from tests.test_gpu_partial import upload as upload_partial
 
 pytestmark = pytest.mark.gpu
 
-# Workspace bytes every call reserves up front (the fixed zeroed region).
-ZERO = 74496
+# Workspace bytes every call reserves up front (the slice counters).
+ZERO = 8192
 
 
 def slices_of(head, B, H):
     """K slices of a head, read back from its token workspace size: past the
-    zeroed region (and, for 33-64 rows, the hidden rows packed per 32-deep
+    counter region (and, for 33-64 rows, the hidden rows packed per 32-deep
     step, 4 KB per step), each slice holds one fp32 partial tile (rows per
     group x 128 columns) per tile of the tile capacity (lanes sized for the
-    largest cache-line shift of 56 columns)."""
+    largest cache-line shift of 56 columns); last come the (row, tile) pairs
+    of the combine launch."""
     rpg = 16 if B <= 16 else (32 if B <= 32 else 64)
     T = sum((head.lane_off[i + 1] - head.lane_off[i] + 56 + 127) // 128
             for i in range(len(head.lane_off) - 1))
     packed = (H + 31) // 32 * 4096 if 32 < B <= 64 else 0
-    extra = sb.sb_workspace_bytes(head, sb.SB_SURF_TOKENS) - ZERO - packed
+    pairs = (B * T * 8 + 255) // 256 * 256
+    extra = sb.sb_workspace_bytes(head, sb.SB_SURF_TOKENS) - ZERO - packed - pairs
     assert extra % (T * rpg * 128 * 4) == 0
     return max(1, extra // (T * rpg * 128 * 4))
 
@@ -119,7 +121,7 @@ def _ids_and_lse(d, head, surface, ws):
 
 
 def test_one_workspace_for_every_shape_surface_and_entry_point(require_gpu):
-    """One workspace, zero-filled once, serves a sequence of calls whose
+    """One workspace serves a sequence of calls whose
     regions grow and shrink: small and large batches, few and many lanes,
     split and unsplit heads, the full-logit plan (which fills most of the
     workspace with shards) and partial completion in between."""
@@ -151,7 +153,7 @@ def test_one_workspace_for_every_shape_surface_and_entry_point(require_gpu):
         s = {"tokens": sb.SB_SURF_TOKENS, "logprobs": sb.SB_SURF_LOGPROBS,
              "full": sb.SB_SURF_FULL_LOGITS}[surf]
         need = max(need, sb.sb_workspace_bytes(head, s))
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
     for (surf, B, H, V, k), h in zip(calls, heads):
         print(f"shared workspace: {surf} B={B} H={H} V={V} k={k}", flush=True)
         if surf == "partial":
