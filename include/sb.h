@@ -157,6 +157,29 @@ sb_status sb_project_tokens(const sb_head_desc *desc, int32_t *ids,
                             void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * sb_project_tokens for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same launches and bit-identical ids, with the workspace
+ * taken from a static device array inside the library instead of an
+ * argument.  The array holds SB_STATIC_SCRATCH_BYTES bytes on every device
+ * the library runs on and stays allocated until the process ends; this call
+ * allocates nothing.  Its address is looked up once per device, on the first
+ * call there.
+ *   ids     DEVICE int32 [B]
+ *   stream  as for every call; the array used is the one of the stream's
+ *           device
+ * Returns SB_ERR_WORKSPACE when the call needs more than
+ * SB_STATIC_SCRATCH_BYTES of workspace (sb_workspace_bytes(desc,
+ * SB_SURF_TOKENS); for example B = 2048 rows at V = 151936 need about 20 MB).
+ * Every call on a device shares that device's array and leaves its last
+ * contents there: calls on one device whose work overlaps in time (two
+ * streams, or two threads, without ordering between them) race and give
+ * undefined results.
+ */
+#define SB_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+sb_status sb_project_tokens_static(const sb_head_desc *desc, int32_t *ids, void *stream);
+
+/*
  * Token surface plus each lane's own result (SemBridge Figure 1 caption and
  * section 5.2: under source projection every lane ships one int32 result per
  * row).  Same launches and same ids as sb_project_tokens; in addition

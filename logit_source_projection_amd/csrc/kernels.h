@@ -221,4 +221,15 @@ hipError_t launch_partial_gemm(const PartialArgs &a, hipStream_t s);
 hipError_t launch_partial_reduce(const PartialArgs &a, int op, float *out, int64_t ldo,
                                  hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Static device scratch for the token call that allocates nothing
+// (sb_project_tokens_static): one array per device, held until the process
+// ends.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+
+// The device address of the current device's scratch array, looked up once
+// per device (hipGetSymbolAddress with that device current) and kept.
+hipError_t static_scratch(int device, void **ptr);
+
 }  // namespace sbk

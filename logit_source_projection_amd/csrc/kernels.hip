@@ -1708,4 +1708,48 @@ hipError_t launch_partial_reduce(const PartialArgs &a, int op, float *out, int64
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch of sb_project_tokens_static.  In host code the array's name
+// is only a stand-in for its device address: the address of each device's
+// copy comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kScratchDevices = 64;
+
+hipError_t static_scratch(int device, void **ptr)
+{
+    static std::atomic<void *> addr[kScratchDevices];  // zero-initialised
+    const bool cached = device >= 0 && device < kScratchDevices;
+    if (cached) {
+        void *p = addr[device].load(std::memory_order_acquire);
+        if (p) {
+            *ptr = p;
+            return hipSuccess;
+        }
+    }
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess)
+        return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess)
+        return e;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess)
+            e = e2;
+    }
+    if (e != hipSuccess)
+        return e;
+    if (!p)
+        return hipErrorInvalidSymbol;
+    if (cached)
+        addr[device].store(p, std::memory_order_release);  // racing first calls store the same
+    *ptr = p;
+    return hipSuccess;
+}
+
 }  // namespace sbk

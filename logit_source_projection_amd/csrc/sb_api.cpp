@@ -345,6 +345,29 @@ sb_status sb_project_tokens(const sb_head_desc *desc, int32_t *ids, void *ws, si
     return project_tokens(desc, ids, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
+sb_status sb_project_tokens_static(const sb_head_desc *desc, int32_t *ids, void *stream)
+{
+    sb_status st = check_desc(desc);
+    if (st != SB_OK)
+        return st;
+    if (desc->B == 0)
+        return SB_OK;
+    if (!ids)
+        return SB_ERR_NULL;
+    const Layout L = layout(desc, SB_SURF_TOKENS);
+    if (L.total > sbk::kStaticScratchBytes)
+        return SB_ERR_WORKSPACE;
+    // the stream's device (the current one for the null stream)
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess)
+        return SB_ERR_HIP;
+    void *ws = nullptr;
+    if (sbk::static_scratch(dev, &ws) != hipSuccess)
+        return SB_ERR_HIP;
+    return project_tokens(desc, ids, nullptr, nullptr, ws, sbk::kStaticScratchBytes, stream);
+}
+
 sb_status sb_project_lane_results(const sb_head_desc *desc, int32_t *ids, int32_t *lane_ids,
                                   float *lane_max, void *ws, size_t ws_bytes, void *stream)
 {

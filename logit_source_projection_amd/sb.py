@@ -37,7 +37,8 @@ SB_RED_MIN = 2
 SB_RED_MAX = 3
 REDUCE_OPS = {"sum": SB_RED_SUM, "prod": SB_RED_PROD, "min": SB_RED_MIN, "max": SB_RED_MAX}
 
-EXPORTS = ("sb_workspace_bytes", "sb_project_tokens", "sb_project_lane_results",
+EXPORTS = ("sb_workspace_bytes", "sb_project_tokens", "sb_project_tokens_static",
+           "sb_project_lane_results",
            "sb_project_logprobs", "sb_full_logits", "sb_partial_workspace_bytes",
            "sb_partial_complete", "sb_status_string")
 
@@ -86,6 +87,8 @@ def lib():
     L.sb_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     L.sb_project_tokens.restype = ctypes.c_int
     L.sb_project_tokens.argtypes = [P, vp, vp, sz, vp]
+    L.sb_project_tokens_static.restype = ctypes.c_int
+    L.sb_project_tokens_static.argtypes = [P, vp, vp]
     L.sb_project_lane_results.restype = ctypes.c_int
     L.sb_project_lane_results.argtypes = [P, vp, vp, vp, vp, sz, vp]
     L.sb_project_logprobs.restype = ctypes.c_int
@@ -217,6 +220,17 @@ def sb_project_tokens(head, ids, ws=None, stream=None):
     _check(lib().sb_project_tokens(head.ref(), _ptr(ids), _ptr(ws), ws.numel(),
                                    _stream(stream)), "sb_project_tokens")
     return ids
+
+
+def sb_project_tokens_static(head, ids, stream=None):
+    """Token-only surface with the library's static device scratch as the
+    workspace (no allocation; SB_STATIC_SCRATCH_BYTES at most)."""
+    _check(lib().sb_project_tokens_static(head.ref(), _ptr(ids), _stream(stream)),
+           "sb_project_tokens_static")
+    return ids
+
+
+SB_STATIC_SCRATCH_BYTES = 32 << 20
 
 
 def sb_project_lane_results(head, ids, lane_ids=None, lane_max=None, ws=None, stream=None):

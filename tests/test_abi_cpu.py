@@ -211,6 +211,22 @@ def test_lane_results_checks():
                                      None) == sb.SB_OK
 
 
+def test_static_scratch_call_checks():
+    """The no-allocation token call validates like sb_project_tokens and
+    refuses, before touching the device, a call whose workspace would not fit
+    its static array."""
+    L = sb.lib()
+    assert L.sb_project_tokens_static(fake_head(B=-1).ref(), FAKE, None) == sb.SB_ERR_SHAPE
+    assert L.sb_project_tokens_static(fake_head().ref(), None, None) == sb.SB_ERR_NULL
+    assert L.sb_project_tokens_static(fake_head(B=0, x_ptr=0).ref(), None, None) == sb.SB_OK
+    big = fake_head(B=4096, H=64, V=151936, off=(0, 37984, 75968, 113952, 151936))
+    assert sb.sb_workspace_bytes(big, sb.SB_SURF_TOKENS) > sb.SB_STATIC_SCRATCH_BYTES
+    assert L.sb_project_tokens_static(big.ref(), FAKE, None) == sb.SB_ERR_WORKSPACE
+    text = open(os.path.join(ROOT, "include", "sb.h")).read()
+    assert "#define SB_STATIC_SCRATCH_BYTES ((size_t)32 << 20)" in text
+    assert sb.SB_STATIC_SCRATCH_BYTES == 32 << 20
+
+
 def test_too_many_lanes():
     V = 8 * 65
     off = list(range(0, V + 1, 8))
