@@ -123,19 +123,18 @@ def record_traffic(args):
     """Scale the call's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the
     same counters read for the plain copy of known size run in the same
     process, and store the bytes per call in the traffic file.  A head call
-    of at most 128 rows is one head-GEMM launch, preceded for 33-64 rows by
-    the hidden-row pack; the partial-completion call is the partial GEMM plus
-    the lane reduction.  The per-dispatch averages of a call's kernels are
-    added."""
+    of at most 128 rows is the head-GEMM launch and the combine launch,
+    preceded for 33-64 rows by the hidden-row pack and for a split head by
+    the clearing of its slice counters; the partial-completion call is the
+    partial GEMM plus the lane reduction.  The per-dispatch averages of a
+    call's kernels are added."""
     from logit_source_projection_amd import inputs
     d = (inputs.PARTIAL_WORKLOADS if args.workload == "mlp_down" else inputs.WORKLOADS)[args.workload]
     B = args.B if args.B is not None else d[0]
     if args.workload == "mlp_down":
         kernel_tags = ("partial_gemm", "partial_reduce")
-    elif 32 < B <= 64:
-        kernel_tags = ("pack_hidden", "head_gemm")
     else:
-        kernel_tags = ("head_gemm",)
+        kernel_tags = ("pack_hidden", "clear_kernel", "head_gemm", "combine_kernel")
     calib = args.copy_calibration_mib << 20
     if calib <= 0:
         sys.exit("--record-traffic needs the --copy-calibration-mib of the profiled run")
@@ -149,6 +148,8 @@ def record_traffic(args):
         for tag in kernel_tags:
             found = {k: vs for k, vs in per.items() if tag in k}
             if not found:
+                if tag in ("pack_hidden", "clear_kernel"):
+                    continue  # launched only for 33-64 rows / split heads
                 sys.exit(f"{path}: no dispatch of {tag}")
             name, vals = max(found.items(), key=lambda kv: len(kv[1]))
             names.append(name)
@@ -487,11 +488,12 @@ def main():
     rows_s = B / (ms * 1e-3)
     nbytes = algorithmic_bytes(d, args.surface)
     achieved = nbytes / (ms * 1e-3) / 1e9
-    one_launch = B <= 128 and args.surface in ("tokens", "logprobs")  # no combine kernel
-    if one_launch and 32 < B <= 64:
-        kernel = "whole call: hidden-row pack (1 MB) + head_gemm_kernel"
-    elif one_launch:
-        kernel = "head_gemm_kernel (the whole call is this one launch)"
+    # HIP events bracket the whole call, so `achieved` is the call's rate: a
+    # lower bound on the head kernel's own rate (the combine launch that
+    # follows it is a few microseconds; rocprofv3 gives both kernels apart).
+    if B <= 128 and args.surface in ("tokens", "logprobs"):
+        kernel = ("whole call: head_gemm_kernel + combine_kernel"
+                  + (" (after the hidden-row pack)" if 32 < B <= 64 else ""))
     else:
         kernel = "whole call (head GEMM and its follow-up kernels)"
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",

@@ -53,31 +53,39 @@ def _record(tmp_path, monkeypatch, workload, fetch, write, B=None, mib=1):
 def test_traffic_is_scaled_by_the_calibration_copy(tmp_path, monkeypatch):
     # A 1 MiB copy that FETCH_SIZE reads as 512 KiB (factor 2) and WRITE_SIZE
     # as 1024 KiB (factor 1); a small input upload that is also a copy; two
-    # head dispatches whose instances sum to 100 and 102 KiB.
+    # calls of a head dispatch (instances summing to 100 and 102 KiB) and its
+    # combine dispatch (2 KiB).
     head = "void sbk::head_gemm_kernel<1, 0, 2, false>(sbk::HeadArgs)"
-    fetch = [(COPY, [3.0]), (COPY, [256.0, 256.0]), (head, [60.0, 40.0]), (head, [50.0, 52.0])]
-    write = [(COPY, [1.0]), (COPY, [512.0, 512.0]), (head, [4.0, 1.0]), (head, [3.0, 2.0])]
+    comb = "sbk::combine_kernel(HIP_vector_type<int, 2u> const*, ...)"
+    fetch = [(COPY, [3.0]), (COPY, [256.0, 256.0]), (head, [60.0, 40.0]), (comb, [1.0, 1.0]),
+             (head, [50.0, 52.0]), (comb, [2.0])]
+    write = [(COPY, [1.0]), (COPY, [512.0, 512.0]), (head, [4.0, 1.0]), (comb, [0.5]),
+             (head, [3.0, 2.0]), (comb, [0.5])]
     rec = _record(tmp_path, monkeypatch, "dense_decode", fetch, write)
     assert rec["kernel_source_sha256"] == bench.kernel_source_hash()
     e = rec["workloads"]["dense_decode/tokens/B16"]
     assert e["fetch_factor"] == 2.0 and e["write_factor"] == 1.0
-    assert e["fetch_bytes"] == 101 * 1024 * 2
-    assert e["write_bytes"] == 5 * 1024
+    assert "head_gemm" in e["kernel"] and "combine_kernel" in e["kernel"]
+    assert e["fetch_bytes"] == 103 * 1024 * 2
+    assert e["write_bytes"] == int(5.5 * 1024)
     assert e["dispatches"] == 2
-    assert bench.recorded_traffic("dense_decode", "tokens", 16) == 101 * 2048 + 5 * 1024
+    assert bench.recorded_traffic("dense_decode", "tokens", 16) == 103 * 2048 + int(5.5 * 1024)
     assert bench.recorded_traffic("dense_decode", "tokens", 8) is None
 
 
 def test_traffic_of_33_to_64_rows_adds_the_hidden_row_pack(tmp_path, monkeypatch):
     pack = "void sbk::pack_hidden_kernel<4>(unsigned short const*, long, int, int, unsigned short*)"
     head = "void sbk::head_gemm_kernel<4, 0, 2, true>(sbk::HeadArgs)"
-    fetch = [(COPY, [512.0]), (pack, [1.0]), (head, [200.0]), (pack, [1.0]), (head, [200.0])]
-    write = [(COPY, [1024.0]), (pack, [0.5]), (head, [2.0]), (pack, [0.5]), (head, [2.0])]
+    comb = "sbk::combine_kernel(HIP_vector_type<int, 2u> const*, ...)"
+    fetch = [(COPY, [512.0]), (pack, [1.0]), (head, [200.0]), (comb, [1.0]),
+             (pack, [1.0]), (head, [200.0]), (comb, [1.0])]
+    write = [(COPY, [1024.0]), (pack, [0.5]), (head, [2.0]), (comb, [0.25]),
+             (pack, [0.5]), (head, [2.0]), (comb, [0.25])]
     rec = _record(tmp_path, monkeypatch, "moe_decode", fetch, write)
     e = rec["workloads"]["moe_decode/tokens/B64"]
     assert "pack_hidden" in e["kernel"] and "head_gemm" in e["kernel"]
-    assert e["fetch_bytes"] == 201 * 1024 * 2
-    assert e["write_bytes"] == int(2.5 * 1024)
+    assert e["fetch_bytes"] == 202 * 1024 * 2
+    assert e["write_bytes"] == int(2.75 * 1024)
 
 
 def test_traffic_without_the_head_kernel_is_refused(tmp_path, monkeypatch):
