@@ -53,6 +53,25 @@ def pin_ids_exact(logits_fn, project_fn, x, w, lane_off):
         assert int(r["ids"][b]) == exact_argmax(ze[b]), b
 
 
+def pin_lanes_exact(logits_fn, project_fn, x, w, lane_off):
+    """Per-lane results against the exact rationals: lane_arg is the lowest
+    global index of the exact maximum inside the lane, lane_max that maximum
+    (within the fp64 error of a sum of H exact products), and the lane
+    sum-exp is sum exp(z - lane_max) over the lane."""
+    z = logits_fn(x, w)
+    r = project_fn(z, lane_off)
+    ze = exact_logits(x, w)
+    for b in range(x.shape[0]):
+        tol = _fp64_bound(x, w, b) + 1e-300
+        for i in range(len(lane_off) - 1):
+            seg = ze[b][lane_off[i]:lane_off[i + 1]]
+            best = max(seg)
+            assert int(r["lane_arg"][b, i]) == lane_off[i] + seg.index(best), (b, i)
+            assert abs(float(r["lane_max"][b, i]) - float(best)) <= tol, (b, i)
+            se = math.fsum(math.exp(float(q - best)) for q in seg)
+            assert abs(float(r["lane_sumexp"][b, i]) - se) <= 1e-12 * se, (b, i)
+
+
 def _fp64_bound(x, w, b):
     """Largest error bound over row b of an fp64 sum of H exact products."""
     H = x.shape[1]
@@ -168,6 +187,21 @@ def test_ids_match_exact_argmax(B, H, V, off, seed):
 def test_top2_gap_and_near_tie_match_exact_rationals(B, H, V, off, seed):
     x, w = tiny_head(B, H, V, seed)
     pin_gap_exact(oracle.logits, oracle.project, x, w, off)
+
+
+@pytest.mark.parametrize("B,H,V,off,seed", TINY_CASES)
+def test_lane_results_match_exact_rationals(B, H, V, off, seed):
+    x, w = tiny_head(B, H, V, seed)
+    pin_lanes_exact(oracle.logits, oracle.project, x, w, off)
+
+
+def test_lane_results_with_ties_inside_and_across_lanes():
+    B, H, V = 3, 32, 64
+    x, w = tiny_head(B, H, V, 7)
+    off = [0, 20, 41, 64]
+    inputs.plant_equal_columns(x, w, 2, (50, 30, 5), 40.0)  # one tied column per lane
+    inputs.plant_equal_columns(x, w, 0, (39, 22), 40.0)     # a tie inside lane 1
+    pin_lanes_exact(oracle.logits, oracle.project, x, w, off)
 
 
 def test_near_tie_threshold_rows():
@@ -449,3 +483,33 @@ def test_mutation_wrong_threshold_factor_is_caught(factor):
         return gap < factor * np.abs(z).max(axis=1)
     bad = _with_gap(oracle.top2_gap, wrong)
     assert _fails(lambda: pin_near_tie_threshold(oracle.logits, bad))
+
+
+def test_mutation_lane_arg_highest_index_is_caught():
+    x, w = tiny_head(3, 32, 64, 7)
+    inputs.plant_equal_columns(x, w, 0, (39, 22), 40.0)
+
+    def bad_project(z, off):
+        r = dict(oracle.project(z, off))
+        A = r["lane_arg"].copy()
+        for i in range(len(off) - 1):
+            seg = z[:, off[i]:off[i + 1]][:, ::-1]
+            A[:, i] = off[i + 1] - 1 - np.argmax(seg, axis=1)
+        r["lane_arg"] = A
+        return r
+    assert _fails(lambda: pin_lanes_exact(oracle.logits, bad_project, x, w, [0, 20, 41, 64]))
+
+
+def test_mutation_lane_boundary_shift_is_caught():
+    x, w = tiny_head(3, 32, 64, 8)
+    # each row's largest logit on the first column of a lane
+    inputs.plant_equal_columns(x, w, 0, (20,), 40.0)
+    inputs.plant_equal_columns(x, w, 1, (41,), 40.0)
+
+    def bad_project(z, off):
+        shifted = [off[0]] + [o + 1 for o in off[1:-1]] + [off[-1]]
+        r = dict(oracle.project(z, off))
+        r2 = oracle.project(z, shifted)
+        r["lane_arg"], r["lane_max"] = r2["lane_arg"], r2["lane_max"]
+        return r
+    assert _fails(lambda: pin_lanes_exact(oracle.logits, bad_project, x, w, [0, 20, 41, 64]))
