@@ -125,8 +125,9 @@ def record_traffic(args):
     process, and store the bytes per call in the traffic file.  A head call
     of at most 128 rows is the head-GEMM launch and the combine launch,
     preceded for 33-64 rows by the hidden-row pack and for a split head by
-    the clearing of its slice counters; the partial-completion call is the
-    partial GEMM plus the lane reduction.  The per-dispatch averages of a
+    the clearing of its slice counters, and followed for complete log-probs
+    by the normalize pass; the partial-completion call is the partial GEMM
+    plus the lane reduction.  The per-dispatch averages of a
     call's kernels are added."""
     from logit_source_projection_amd import inputs
     d = (inputs.PARTIAL_WORKLOADS if args.workload == "mlp_down" else inputs.WORKLOADS)[args.workload]
@@ -134,7 +135,8 @@ def record_traffic(args):
     if args.workload == "mlp_down":
         kernel_tags = ("partial_gemm", "partial_reduce")
     else:
-        kernel_tags = ("pack_hidden", "clear_kernel", "head_gemm", "combine_kernel")
+        kernel_tags = ("pack_hidden", "clear_kernel", "head_gemm", "combine_kernel",
+                       "normalize_kernel")
     calib = args.copy_calibration_mib << 20
     if calib <= 0:
         sys.exit("--record-traffic needs the --copy-calibration-mib of the profiled run")
@@ -148,8 +150,8 @@ def record_traffic(args):
         for tag in kernel_tags:
             found = {k: vs for k, vs in per.items() if tag in k}
             if not found:
-                if tag in ("pack_hidden", "clear_kernel"):
-                    continue  # launched only for 33-64 rows / split heads
+                if tag in ("pack_hidden", "clear_kernel", "normalize_kernel"):
+                    continue  # only for 33-64 rows / split heads / complete log-probs
                 sys.exit(f"{path}: no dispatch of {tag}")
             name, vals = max(found.items(), key=lambda kv: len(kv[1]))
             names.append(name)
@@ -504,8 +506,10 @@ def main():
     if args.workload == "prefill":
         tf = flops(d) / (ms * 1e-3) / 1e12
         roofline = dict(bound="mfma", achieved=round(tf, 1), peak=BF16_PEAK_TFLOPS,
-                        unit="TFLOP/s", frac=round(tf / BF16_PEAK_TFLOPS, 4), traffic=None,
-                        kernel="head GEMM (whole call)", algorithmic_flops=flops(d))
+                        unit="TFLOP/s", frac=round(tf / BF16_PEAK_TFLOPS, 4),
+                        traffic=recorded_traffic(args.workload, args.surface, B),
+                        kernel="whole call (head GEMM and its follow-up kernels)",
+                        algorithmic_flops=flops(d), algorithmic_bytes=nbytes)
 
     report = {}
     if not args.no_report:
