@@ -285,7 +285,7 @@ __device__ __forceinline__ void emit_tile_row(const HeadArgs &a, const float (&y
 // .. + 7] (zeros past B rows and past H), so that a wave's fragment load of
 // a step reads MB contiguous KB instead of 16 half cache lines per row block.
 // Positions past H in a row are never read.
-// Zero the call's counters and keys: every thread of the grid takes words
+// Zero the call's slice counters: every thread of the grid takes words
 // i, i + stride, ... of each range.
 __device__ __forceinline__ void clear_ranges(const ZeroRanges &z, int64_t i, int64_t stride)
 {
@@ -1331,7 +1331,7 @@ hipError_t launch_mb(const HeadArgs &a, int epi, hipStream_t s)
     dim3 grid(((ntiles + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg) * a.kslices);
     const int nsteps = (a.H + kStepK - 1) / kStepK;
     if (XP && nsteps > 0) {
-        // the pack launch also clears the call's counters and keys
+        // the pack launch also clears the call's slice counters
         hipLaunchKernelGGL(pack_hidden_kernel<MB>, dim3(nsteps), dim3(MB * 64), 0, s, a.x,
                            a.ldx, a.B, a.H, a.xp, a.zero);
         const hipError_t e = hipGetLastError();

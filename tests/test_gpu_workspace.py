@@ -1,11 +1,13 @@
 """GPU tests of the workspace contract: its contents on entry do not matter.
 
-Every call clears the completion counters, lane keys and slice counters it
-relies on before its head kernel runs, so a workspace full of garbage -- a
-caller's mistake, memory reused from other work, or a call that failed
-after part of its work was enqueued -- gives the same results, bit for bit,
-as a freshly zeroed one.  No kernel waits on these counters, so garbage in
-them cannot stall a launch; at worst it would misplace the completion step,
+The head kernels write every per-(row, tile) pair and every partial tile
+before the combine and fold steps read them, and the only state a call
+carries between workgroups -- the K-slice counters -- is cleared by the
+call itself before its head kernel runs.  So a workspace full of garbage
+(a caller's mistake, memory reused from other work, or a call that failed
+after part of its work was enqueued) must give the same results, bit for
+bit, as a freshly allocated one.  No kernel waits on a counter, so garbage
+cannot stall a launch; at worst a stale counter would misplace a fold,
 which these tests would see as wrong or unwritten outputs.
 """
 import numpy as np
