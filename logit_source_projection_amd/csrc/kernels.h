@@ -66,7 +66,7 @@ struct HeadArgs {
     // finish a tile adds the kslices partials in slice order.
     int32_t kslices;             // 1 = no split
     int32_t slice_steps;         // kStepK-row steps per slice, a multiple of kWaves
-    float *kpart;                // [T][kslices][rows per group][kTileN] fp32 partial tiles
+    float *kpart;                // [T][kslices][row blocks][2][threads][4] fp32 partial tiles
     uint32_t *kctr;              // [T] per-tile slice counters, cleared before the launch
     // Hidden rows packed per K step for 33-64 rows (one row group of four
     // blocks): [steps][4][64 lanes] 16-byte units, written by the call.

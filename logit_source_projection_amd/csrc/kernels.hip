@@ -117,13 +117,17 @@ __device__ __forceinline__ void lse_merge(float &m1, float &s1, float m2, float 
 }
 
 // Results read by another workgroup of the same launch are written through
-// to memory (system-scope relaxed atomic stores are never left dirty in an
-// XCD's L2), so publishing them needs only a wait for store completion -- no
-// L2 write-back fence in every workgroup.
-__device__ __forceinline__ void store_through(void *p, uint32_t lo, uint32_t hi)
+// to memory (the sc0 and sc1 bits of the store: never left dirty in an XCD's
+// L2), so publishing them needs only a wait for store completion -- no L2
+// write-back fence in every workgroup.
+constexpr int kPolicyWriteThrough = 1 | 16;  // sc0 | sc1 of a buffer instruction
+
+__device__ __forceinline__ void store16_through(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                const float *v)
 {
-    const uint64_t v = (uint64_t)lo | ((uint64_t)hi << 32);
-    __hip_atomic_store(static_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const u32x4 u = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                     __float_as_uint(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, voff, 0, kPolicyWriteThrough);
 }
 
 // All of this wave's memory operations have completed.
@@ -432,6 +436,11 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
         compute_step<MB>(fa, acc, k0, H, g);
 
     // ---------------- epilogue, one 16-row block at a time ----------------
+    // A K slice's partial tile: kPartBlock floats, one row block after the
+    // other, each as two halves of one 16-byte unit per thread.
+    constexpr int kPartBlock = kRowBlock * MB * kTileN;
+    constexpr int kPartHalf = kRowBlock * kTileN / 2;
+    static_assert(kPartHalf == 4 * kThreads, "a half holds 4 floats per thread");
     const int erow = threadIdx.x >> 4;  // 0..15: row inside the block
     const int cg = threadIdx.x & 15;    // 8-column group inside the tile
     const int colrel = c0 + 8 * cg;     // column inside the lane
@@ -470,12 +479,16 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
         const bool rowok = b < a.B;
 
         if (a.kslices > 1) {
-            // this slice's partial tile, written through for the last slice
-            float *p = a.kpart + ((size_t)tile * a.kslices + slice) * (kRowBlock * MB * kTileN) +
-                       (kRowBlock * mb + erow) * kTileN + 8 * cg;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                store_through(p + 2 * j, __float_as_uint(y[2 * j]), __float_as_uint(y[2 * j + 1]));
+            // This slice's partial tile, written through for the workgroup
+            // that folds the tile.  A thread's 8 values of row block mb are
+            // two 16-byte units at [mb][half][thread], so each store
+            // instruction of a wave writes 1 KB of contiguous memory.
+            const __amdgpu_buffer_rsrc_t r =
+                make_rsrc(a.kpart + ((size_t)tile * a.kslices + slice) * kPartBlock,
+                          (int64_t)kPartBlock * sizeof(float));
+            const uint32_t vo = (uint32_t)(mb * kRowBlock * kTileN + 4 * threadIdx.x) * 4u;
+            store16_through(r, vo, y);
+            store16_through(r, vo + kPartHalf * 4u, y + 4);
             continue;
         }
         emit_tile_row<EPI>(a, y, b, rowok, lane, tile, colrel, nvalid, gcol0 + 8 * cg, cg);
@@ -498,14 +511,14 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
         for (int mb = 0; mb < MB; ++mb) {
             if (m0 + kRowBlock * mb >= a.B)
                 break;
-            const float *p = a.kpart + (size_t)tile * a.kslices * (kRowBlock * MB * kTileN) +
-                             (kRowBlock * mb + erow) * kTileN + 8 * cg;
+            const float *p = a.kpart + (size_t)tile * a.kslices * kPartBlock +
+                             mb * kRowBlock * kTileN + 4 * threadIdx.x;
             f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
-            f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 4);
+            f32x4 hi = *reinterpret_cast<const f32x4 *>(p + kPartHalf);
             for (int sl = 1; sl < a.kslices; ++sl) {
-                p += kRowBlock * MB * kTileN;
+                p += kPartBlock;
                 lo += *reinterpret_cast<const f32x4 *>(p);
-                hi += *reinterpret_cast<const f32x4 *>(p + 4);
+                hi += *reinterpret_cast<const f32x4 *>(p + kPartHalf);
             }
             const float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             const int b = m0 + kRowBlock * mb + erow;

@@ -110,7 +110,7 @@ Layout layout(const sb_head_desc *d, int surface)
     at = kCtrBytes;
     L.kslices = sbk::k_slices(d->B, d->H, d->V);
     if (L.kslices > 1) {
-        // partial tiles of the K slices, [T][kslices][rows per group][kTileN]
+        // partial tiles of the K slices: T x kslices tiles of rows per group x kTileN fp32
         L.kpart = at;
         at = align_up(at + (size_t)L.T * L.kslices * rpg * sbk::kTileN * sizeof(float),
                       kRegionAlign);
