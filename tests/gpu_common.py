@@ -24,7 +24,9 @@ def upload(d, device="cuda", lanes_separate=False, pad_w=0, pad_x=0, pad_bits=0x
            lane_base_bytes=None):
     """Device tensors for a workload dict; optionally each lane in its own
     allocation and/or row padding filled with ``pad_bits`` (NaN by default)
-    that the kernels must never use.  ``lane_base_bytes`` (with separate
+    that the kernels must never use.  One weight allocation whose width is
+    not a multiple of 8 is padded to the next multiple (the ABI's stride
+    rule).  ``lane_base_bytes`` (with separate
     lanes) starts lane i's shard that many bytes (a multiple of 16) into its
     allocation, which the caching allocator aligns to at least 512 bytes."""
     x_bits, w_bits, off = d["x"], d["w"], d["lane_off"]
@@ -53,6 +55,13 @@ def upload(d, device="cuda", lanes_separate=False, pad_w=0, pad_x=0, pad_bits=0x
             assert t.data_ptr() % 128 == lane_base_bytes[i] % 128
             shards.append(t[:, :wi])
         w = shards
+    elif pad_w or w_bits.shape[1] % 8:
+        # one allocation at a row stride of a multiple of 8 plus pad_w
+        V = w_bits.shape[1]
+        ldw = (V + 7) // 8 * 8 + pad_w
+        wp = np.full((H, ldw), pad_bits, dtype=np.uint16)
+        wp[:, :V] = w_bits
+        w = sb.to_device_bf16(wp, device)[:, :V]
     else:
         w = sb.to_device_bf16(w_bits, device)
     return sb.Head(x, w, off)
