@@ -137,3 +137,30 @@ def test_mlp_down_workload(require_gpu, B):
     for op in opart.OPS:
         worst[op] = float(check(run(part, op), P, op).max())
     print("worst relative error per operator:", worst, flush=True)
+
+
+def draw_partial_case(i):
+    """Sweep case i: rows weighted to the dispatch boundaries, 1-6 lanes of
+    ragged K (down to one row), ragged N, weight scale and row padding."""
+    rng = np.random.default_rng([2025, i])
+    B = int(rng.choice([1, 2, 15, 16, 17, 31, 32, 33, 64, 65, 128, 129, 300]))
+    k = int(rng.integers(1, 7))
+    Ks = tuple(int(rng.integers(1, 2500)) if rng.random() < 0.9 else int(rng.integers(1, 9))
+               for _ in range(k))
+    nmax = max(1, min(1500, int(1e8 // (B * sum(Ks)))))
+    N = int(rng.integers(1, nmax + 1))
+    sigma_w = float(rng.choice([0.005, 0.05, 0.5]))
+    pad_x, pad_w = 8 * int(rng.integers(0, 3)), 8 * int(rng.integers(0, 3))
+    return B, Ks, N, sigma_w, pad_x, pad_w
+
+
+@pytest.mark.parametrize("i", range(60))
+def test_partial_completion_sweep(require_gpu, i):
+    B, Ks, N, sigma_w, pad_x, pad_w = draw_partial_case(i)
+    print(f"partial sweep case {i}: B={B} Ks={Ks} N={N} sigma_w={sigma_w} "
+          f"pad=({pad_x}, {pad_w})", flush=True)
+    xs, ws = inputs.draw_partial(B, N, Ks, seed=4000 + i, sigma_w=sigma_w)
+    P = opart.partials(xs, ws)
+    part = upload(xs, ws, pad_x=pad_x, pad_w=pad_w)
+    for op in opart.OPS:
+        check(run(part, op), P, op)
