@@ -116,6 +116,103 @@ __device__ __forceinline__ void lse_merge(float &m1, float &s1, float m2, float 
     }
 }
 
+// Cross-lane reductions inside the 16-lane rows of a wave use DPP moves (a
+// VALU operand modifier: no LDS traffic, no address registers).  Four steps
+// pair each lane with one in the other half of a group of 2, 4, 8 and 16
+// lanes: quad swaps by 1 and by 2, then the mirror of each 8-lane half and of
+// the 16-lane row.  Both reductions below are symmetric in their two
+// operands (floating-point addition commutes; the (max, lowest index) choice
+// is a total order), so every lane of a row ends with the same bits.
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i of its 8-lane half
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15 - i of its row
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_int(int v)
+{
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_float(float v)
+{
+    return __int_as_float(dpp_int<CTRL>(__float_as_int(v)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void best_step(float &bv, int &bi)
+{
+    const float ov = dpp_float<CTRL>(bv);
+    const int oi = dpp_int<CTRL>(bi);
+    if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+    }
+}
+
+// (max, lowest index) over each 16-lane row; every lane gets its row's.
+__device__ __forceinline__ void row16_best(float &bv, int &bi)
+{
+    best_step<kDppQuadXor1>(bv, bi);
+    best_step<kDppQuadXor2>(bv, bi);
+    best_step<kDppHalfMirror>(bv, bi);
+    best_step<kDppMirror>(bv, bi);
+}
+
+// Sum over each 16-lane row; every lane gets its row's.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += dpp_float<kDppQuadXor1>(v);
+    v += dpp_float<kDppQuadXor2>(v);
+    v += dpp_float<kDppHalfMirror>(v);
+    v += dpp_float<kDppMirror>(v);
+    return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void lse_step(float &m, float &s)
+{
+    lse_merge(m, s, dpp_float<CTRL>(m), dpp_float<CTRL>(s));
+}
+
+// Over the whole wave: the rows by DPP, then the four row results (lanes 0,
+// 16, 32, 48) read as wave-uniform values and merged in row order.
+__device__ __forceinline__ void wave_best(float &bv, int &bi)
+{
+    row16_best(bv, bi);
+    float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+    int i = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+        const int oi = __builtin_amdgcn_readlane(bi, 16 * r);
+        if (better(ov, oi, v, i)) {
+            v = ov;
+            i = oi;
+        }
+    }
+    bv = v;
+    bi = i;
+}
+
+// Online logsumexp (m, s) over the whole wave, as wave_best.
+__device__ __forceinline__ void wave_lse(float &m, float &s)
+{
+    lse_step<kDppQuadXor1>(m, s);
+    lse_step<kDppQuadXor2>(m, s);
+    lse_step<kDppHalfMirror>(m, s);
+    lse_step<kDppMirror>(m, s);
+    float wm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0));
+    float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 0));
+#pragma unroll
+    for (int r = 1; r < 4; ++r)
+        lse_merge(wm, ws, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16 * r)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), 16 * r)));
+    m = wm;
+    s = ws;
+}
+
 // Results read by another workgroup of the same launch are written through
 // to memory (the sc0 and sc1 bits of the store: never left dirty in an XCD's
 // L2), so publishing them needs only a wait for store completion -- no L2
@@ -256,24 +353,14 @@ __device__ __forceinline__ void emit_tile_row(const HeadArgs &a, const float (&y
                 bi = gcol + j;
             }
         // across the 16 threads of this row (one 16-lane row of the wave)
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 16);
-            const int oi = __shfl_xor(bi, o, 16);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
+        row16_best(bv, bi);
         float se = 0.f;
         if (EPI != kEpiPair) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 if (j < nvalid)
                     se += __expf(y[j] - bv);
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1)
-                se += __shfl_xor(se, o, 16);
+            se = row16_sum(se);
         }
         if (cg == 0 && rowok) {
             const int64_t idx = (int64_t)b * a.T + tile;
@@ -791,18 +878,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const int2 *pair, con
                     lse_merge(m, s, q[u].x, q[u].y);
             }
         }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, 64);
-            const int oi = __shfl_xor(bi, o, 64);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-            const float om = __shfl_xor(m, o, 64);
-            const float os = __shfl_xor(s, o, 64);
-            lse_merge(m, s, om, os);
-        }
+        wave_best(bv, bi);
+        if (mrow)
+            wave_lse(m, s);
         if (L == 0) {
             lv[lane] = bv + 0.f;  // -0 reported as +0
             li[lane] = bi;
@@ -960,15 +1038,7 @@ __global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float *logit
             }
         }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
+    wave_best(bv, bi);
     const int L = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (L == 0) {
         wv[wave] = bv;
@@ -1278,24 +1348,14 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
                         bv = y[c];
                         bi = gcol + c;
                     }
-#pragma unroll
-                for (int o = 8; o >= 1; o >>= 1) {
-                    const float ov = __shfl_xor(bv, o, 16);
-                    const int oi = __shfl_xor(bi, o, 16);
-                    if (better(ov, oi, bv, bi)) {
-                        bv = ov;
-                        bi = oi;
-                    }
-                }
+                row16_best(bv, bi);
                 float se = 0.f;
                 if (EPI != kEpiPair) {
 #pragma unroll
                     for (int c = 0; c < 8; ++c)
                         if (c < nvalid)
                             se += __expf(y[c] - bv);
-#pragma unroll
-                    for (int o = 8; o >= 1; o >>= 1)
-                        se += __shfl_xor(se, o, 16);
+                    se = row16_sum(se);
                 }
                 if (n == 0 && rowok) {
                     const int64_t idx = (int64_t)b * a.T + tile;
