@@ -28,5 +28,28 @@ def build(verbose=False):
     return LIB
 
 
+DRIVER_SRC = os.path.join(ROOT, "tests", "abi_driver.c")
+DRIVER = os.path.join(ROOT, "tests", "abi_driver")
+
+
+def build_abi_driver(verbose=False):
+    """Compile the plain C program that drives libsb.so through include/sb.h
+    and the HIP runtime alone (a test of the C ABI); C99, gcc.  It finds
+    libsb.so through an rpath relative to itself.  Call after build()."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = DRIVER + ".tmp"
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           DRIVER_SRC, "-o", tmp, "-L", HERE, "-lsb", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../logit_source_projection_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, DRIVER)
+    return DRIVER
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_abi_driver(verbose=True))

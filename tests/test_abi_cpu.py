@@ -350,3 +350,24 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         sb.lib()
     with pytest.raises(RuntimeError, match="libsb.so not found"):
         sb.sb_workspace_bytes(fake_head(), sb.SB_SURF_TOKENS)
+
+
+def test_header_compiles_as_c99():
+    """include/sb.h is a C header: it compiles as strict C99 with every
+    warning an error, with no C++ and no HIP header."""
+    import shutil
+    import tempfile
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    with tempfile.TemporaryDirectory() as t:
+        src = os.path.join(t, "use_sb.c")
+        with open(src, "w") as f:
+            f.write('#include "sb.h"\n'
+                    "int use(const sb_head_desc *d, int32_t *ids) {\n"
+                    "    return (int)sb_project_tokens(d, ids, (void *)0, 0, (void *)0);\n"
+                    "}\n")
+        r = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
+                            "-fsyntax-only", "-I", inc, src], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
