@@ -239,3 +239,16 @@ def test_workspace_reuse_across_shapes(require_gpu):
         ok = ~r["near_tie"]
         assert np.array_equal(ids.cpu().numpy()[ok], r["ids"][ok])
         assert np.allclose(lse.cpu().numpy(), r["lse"], rtol=1e-4)
+
+
+@pytest.mark.parametrize("B,H,V,k", [
+    (1, 32768, 4096, 2),     # one row, 8 K slices of 128 steps
+    (4, 20000, 1500, 2),     # ragged K tail, 8 slices
+    (64, 16384, 3000, 2),    # packed hidden rows (2 MB) and K slices
+    (200, 12288, 600, 3),    # large-batch kernel, 192 K stages
+])
+def test_long_hidden_sums(require_gpu, B, H, V, k):
+    """Hidden sizes of 12k-32k: every slice, stage and fold of a long sum,
+    against the oracle within the row-max-relative logit tolerance."""
+    d = inputs.make_random(B, H, V, inputs.equal_lanes(V, k), seed=H + B, sigma_w=0.01)
+    _case(d, lanes_separate=True)
