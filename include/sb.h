@@ -90,7 +90,8 @@ typedef enum sb_status {
                                 multiple of 4                                  */
     SB_ERR_WORKSPACE = -5,   /* workspace smaller than sb_workspace_bytes()   */
     SB_ERR_UNSUPPORTED = -6, /* B > 65535; or 40 shard rows or 64 rows of x
-                                span 4 GiB or more; or, for B >= 129, 72
+                                span 4 GiB or more; or, for 65 <= B <= 128,
+                                128 rows of x do; or, for B >= 129, 72
                                 shard rows or 256 rows of x do             */
     SB_ERR_HIP = -7          /* a HIP launch failed                            */
 } sb_status;

@@ -14,6 +14,9 @@ FLAGS = [
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
+    # every symbol resolved at link time: a kernel template that failed to
+    # instantiate is an error here, not a library that fails to load
+    "-Wl,-z,defs",
 ]
 
 

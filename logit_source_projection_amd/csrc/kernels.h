@@ -156,16 +156,24 @@ inline int slice_steps(int H, int slices)
 // logits or shards.  a.zero is cleared first, on the same stream.
 hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s);
 
-// Batches of at least this many rows (more than two 64-row groups) use the
-// large-batch (MFMA-bound) head GEMM for every surface.  bench.py timings of
-// both kernels from 65 to 768 rows: the pair kernel is faster up to 128 rows
-// (0.37 against 0.40-0.41 ms on the MoE head at 128), the large kernel from
-// 144 rows on (0.40-0.42 against 0.45 ms at 144, 0.44 against 0.57 ms at 255).
-constexpr int kLargeBatch = 129;
+// Batches of at least this many rows (more than one 64-row group) use the
+// large-batch head GEMM for every surface: from 65 to 128 rows with 128-row
+// blocks (bench.py, alternated with the earlier kernel of two 128-column tiles
+// per 64-row group: 9-12 % faster on the dense and MoE heads), from 129 rows
+// with 256-row blocks (128-row blocks there read the weight once per block
+// row and ran 9-20 % slower from 160 to 2048 rows).
+constexpr int kLargeBatch = 65;
 // Block rows and K stage depth of the large-batch kernel (its 32-bit buffer
-// offsets reach kLargeRows rows of x and kLargeStepK rows of a shard).
+// offsets reach large_block_rows(B) rows of x and at most kLargeStepK rows of
+// a shard).  Up to kLargeSmallMax rows it runs 128-row blocks with
+// kLargeSmallStepK-deep stages in a three-stage LDS ring, beyond that
+// kLargeRows-row blocks with kLargeStepK-deep stages in two.
 constexpr int kLargeRows = 256;
+constexpr int kLargeSmallMax = 128;
 constexpr int kLargeStepK = 64;
+constexpr int kLargeSmallStepK = 32;
+inline int large_block_rows(int B) { return B <= kLargeSmallMax ? 128 : kLargeRows; }
+inline int large_step_k(int B) { return B <= kLargeSmallMax ? kLargeSmallStepK : kLargeStepK; }
 
 // Large-batch head GEMM: writes the (row, tile) results (and logits /
 // shards); ids / lse / sel_lp come from launch_combine afterwards.

@@ -614,226 +614,11 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void head_ge
     }
 }
 
-// ---------------------------------------------------------------------------
-// Head GEMM for more than 64 rows (several row groups of four 16-row blocks):
-// two weight tiles per workgroup that share the hidden-row fragments.
-//
-// With 64 rows per group the hidden-row fragments of a step are half the size
-// of its weight slab, and every workgroup re-reads them through the L2.  Here
-// the 4 waves of a workgroup cover two
-// adjacent 128-column tiles, with the K steps split two ways: wave w computes
-// tile w & 1 over the steps h, h + 2, h + 4, ... of its half h = w >> 1.  The
-// two waves of a half load two of the four row blocks each and exchange them
-// through LDS, so the hidden rows are read once per tile pair.  Each logit is
-// (sum over half 0) + (sum over half 1), each half summed in ascending K
-// order, whatever the tile's position; the three surfaces stay bit-identical.
-// ---------------------------------------------------------------------------
-constexpr int kXRows = kMaxMB * 64;  // u32x4 per (parity, K half): 4 row blocks x 64 lanes
-
-template <int POL>
-__device__ __forceinline__ void load_pair_step(Frags<kMaxMB> &f, const uint16_t *wbase,
-                                               int64_t wbytes, const uint16_t *xbase,
-                                               int64_t xbytes, int k0, int64_t ldw,
-                                               const uint32_t (&wvo)[8], const uint32_t (&xvo)[2])
-{
-    const int64_t wshift = (int64_t)k0 * ldw;
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + wshift, wbytes - wshift * 2);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + k0, xbytes - (int64_t)k0 * 2);
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        f.w[r] = load16w<POL>(rw, wvo[r]);
-    // this wave's half of the hidden-row fragments, exchanged before use
-    f.x[0] = load16(rx, xvo[0]);
-    f.x[1] = load16(rx, xvo[1]);
-}
-
-template <int EPI, int POL>
-__global__ __launch_bounds__(kThreads, Occupancy<kMaxMB>::kBlocksPerCU) void head_gemm_pair_kernel(
-    const HeadArgs a)
-{
-    constexpr int MB = kMaxMB;
-    __shared__ float red[kWaves][kRowBlock][kTileN + 4];
-    __shared__ u32x4 xs[2][2][kXRows];  // [step parity][K half][row block][lane]
-
-    // 1-D grid in blocks of 8 tile pairs x all row groups, as the one-tile kernel
-    const int ntiles = a.lanes.tile0[a.lanes.k];
-    const int npairs = (ntiles + 1) / 2;
-    const int groups = (a.B + kRowBlock * MB - 1) / (kRowBlock * MB);
-    const int q = blockIdx.x >> 3;
-    const int pair = (q / groups) * 8 + (blockIdx.x & 7);
-    const int group = q - (q / groups) * groups;
-    if (pair >= npairs)
-        return;
-    const bool second = 2 * pair + 1 < ntiles;  // the pair's second tile exists
-
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int L = threadIdx.x & 63;
-    const int n = L & 15;
-    const int g = L >> 4;
-    const int t = wave & 1, h = wave >> 1;
-    const int H = a.H;
-    const int m0 = group * (kRowBlock * MB);
-    const int rows_here = min(a.B - m0, kRowBlock * MB);
-
-    // geometry of both tiles (the epilogue handles both); a missing second
-    // tile takes the first one's lane and reads no weight
-    int lane2[2], c02[2], vi2[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int tl = (u == 1 && second) ? 2 * pair + 1 : 2 * pair;
-        lane2[u] = find_lane(a.lanes, tl);
-        vi2[u] = a.lanes.off[lane2[u] + 1] - a.lanes.off[lane2[u]];
-        c02[u] = (tl - a.lanes.tile0[lane2[u]]) * kTileN - a.lanes.shift[lane2[u]];
-    }
-    const int lane = t ? lane2[1] : lane2[0];
-    const int c0 = t ? c02[1] : c02[0];
-    const int Vi = t ? vi2[1] : vi2[0];
-    const bool reads_w = t == 0 || second;
-    const int cb = max(c0, 0);
-    const uint16_t *wbase = a.lanes.w[lane] + cb;
-    const int64_t wcols = ((int64_t)(Vi - cb) + 7) & ~(int64_t)7;
-    const int64_t wbytes = reads_w && H > 0 ? (((int64_t)(H - 1) * a.ldw) + wcols) * 2 : 0;
-    const uint16_t *xbase = a.x + (int64_t)m0 * a.ldx;
-    const int64_t xbytes = H > 0 ? (((int64_t)(rows_here - 1) * a.ldx) + ((H + 7) & ~7)) * 2 : 0;
-
-    uint32_t wvo[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-        wvo[r] = (uint32_t)(((int64_t)(8 * g + r) * a.ldw + max(c0 + 8 * n - cb, 0)) * 2);
-    uint32_t xvo[2];  // row blocks 2t and 2t + 1
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        xvo[j] = (uint32_t)(((int64_t)(kRowBlock * (2 * t + j) + n) * a.ldx + 8 * g) * 2);
-
-    f32x4 acc[MB][8];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-            acc[mb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // This wave's steps are h, h + 2, ...: nw of them.  Every wave runs nmax
-    // exchange steps (one barrier each); steps past H only see masked zeros.
-    const int nsteps = (H + kStepK - 1) / kStepK;
-    const int nmax = (nsteps + 1) / 2;
-    const int nw = nsteps > h ? (nsteps - h + 1) / 2 : 0;
-    constexpr int kStride = 2 * kStepK;
-    Frags<MB> fa, fb;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        fa.w[r] = u32x4{0u, 0u, 0u, 0u};
-        fb.w[r] = u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < MB; ++j) {
-        fa.x[j] = u32x4{0u, 0u, 0u, 0u};
-        fb.x[j] = u32x4{0u, 0u, 0u, 0u};
-    }
-    auto step = [&](Frags<MB> &f, int i, int k0) {
-        // publish this wave's half, then take all four row blocks; parity i
-        // alternates, so a slot is rewritten only after the next barrier
-        u32x4 *slot = &xs[i & 1][h][0];
-        slot[(2 * t) * 64 + L] = f.x[0];
-        slot[(2 * t + 1) * 64 + L] = f.x[1];
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < MB; ++j)
-            f.x[j] = slot[j * 64 + L];
-        compute_step<MB>(f, acc, k0, H, g);
-    };
-    int k0 = h * kStepK;
-    if (nw > 0)
-        load_pair_step<POL>(fa, wbase, wbytes, xbase, xbytes, k0, a.ldw, wvo, xvo);
-    int i = 0;
-    for (; i + 2 <= nmax; i += 2) {
-        if (i + 1 < nw)
-            load_pair_step<POL>(fb, wbase, wbytes, xbase, xbytes, k0 + kStride, a.ldw, wvo, xvo);
-        step(fa, i, k0);
-        if (i + 2 < nw)
-            load_pair_step<POL>(fa, wbase, wbytes, xbase, xbytes, k0 + 2 * kStride, a.ldw, wvo, xvo);
-        step(fb, i + 1, k0 + kStride);
-        k0 += 2 * kStride;
-    }
-    if (nmax & 1)
-        step(fa, i, k0);
-
-    // ---------------- epilogue, one 16-row block at a time ----------------
-    const int erow = threadIdx.x >> 4;  // 0..15: row inside the block
-    const int cg = threadIdx.x & 15;    // 8-column group inside the tile
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        if (m0 + kRowBlock * mb >= a.B)
-            break;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            f32x4 lo = {acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
-            f32x4 hi = {acc[mb][4][r], acc[mb][5][r], acc[mb][6][r], acc[mb][7][r]};
-            *reinterpret_cast<f32x4 *>(&red[wave][4 * g + r][8 * n]) = lo;
-            *reinterpret_cast<f32x4 *>(&red[wave][4 * g + r][8 * n + 4]) = hi;
-        }
-        __syncthreads();
-        // tile u: half 0 in wave u, half 1 in wave u + 2
-        float y[2][8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const f32x4 p0l = *reinterpret_cast<const f32x4 *>(&red[u][erow][8 * cg]);
-            const f32x4 p0h = *reinterpret_cast<const f32x4 *>(&red[u][erow][8 * cg + 4]);
-            const f32x4 p1l = *reinterpret_cast<const f32x4 *>(&red[u + 2][erow][8 * cg]);
-            const f32x4 p1h = *reinterpret_cast<const f32x4 *>(&red[u + 2][erow][8 * cg + 4]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                y[u][j] = p0l[j] + p1l[j];
-                y[u][j + 4] = p0h[j] + p1h[j];
-            }
-        }
-        __syncthreads();  // LDS free for the next block
-
-        const int b = m0 + kRowBlock * mb + erow;
-        const bool rowok = b < a.B;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if (u == 1 && !second)
-                break;
-            const int colrel = c02[u] + 8 * cg;
-            const int nvalid = colrel < 0 ? 0 : max(0, min(8, vi2[u] - colrel));
-            emit_tile_row<EPI>(a, y[u], b, rowok, lane2[u], 2 * pair + u, colrel, nvalid,
-                               a.lanes.off[lane2[u]] + colrel, cg);
-        }
-    }
-}
-
-template <int POL>
-hipError_t launch_pair(const HeadArgs &a, int epi, hipStream_t s)
-{
-    const int rpg = kRowBlock * kMaxMB;
-    const int npairs = (a.lanes.tile0[a.lanes.k] + 1) / 2;
-    dim3 grid(((npairs + 7) / 8) * 8 * ((a.B + rpg - 1) / rpg));
-    const hipError_t e = launch_clear(a.zero, s);
-    if (e != hipSuccess)
-        return e;
-    switch (epi) {
-    case kEpiPair:
-        hipLaunchKernelGGL((head_gemm_pair_kernel<kEpiPair, POL>), grid, dim3(kThreads), 0, s, a);
-        break;
-    case kEpiPairLse:
-        hipLaunchKernelGGL((head_gemm_pair_kernel<kEpiPairLse, POL>), grid, dim3(kThreads), 0, s, a);
-        break;
-    case kEpiPairLseOut:
-        hipLaunchKernelGGL((head_gemm_pair_kernel<kEpiPairLseOut, POL>), grid, dim3(kThreads), 0, s, a);
-        break;
-    case kEpiShard:
-        hipLaunchKernelGGL((head_gemm_pair_kernel<kEpiShard, POL>), grid, dim3(kThreads), 0, s, a);
-        break;
-    default:
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
 // One workgroup per row folds the per-(row, tile) results.  Wave w takes
 // lanes w, w + 4, ...; in a lane, thread j merges tiles t0 + j, t0 + j + 64,
-// ... in ascending order (kCombineBatch loads in flight), and a fixed 64-lane
-// butterfly merges the threads.  The lane results are then folded in
+// ... in ascending order (kCombineBatch loads in flight), and the DPP row
+// steps plus an in-order merge of the four rows combine the threads.  The
+// lane results are then folded in
 // ascending lane order: the ID of the first lane holding the row maximum
 // (lowest index on ties, since lanes ascend), and
 // lse = M + log sum_i S_i exp(M_i - M).  Every order here is fixed by the
@@ -1057,48 +842,67 @@ __global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float *logit
 
 
 // ---------------------------------------------------------------------------
-// Large-batch head GEMM (prefill shapes, MFMA-bound).
+// Large-batch head GEMM (more than 64 rows; MFMA-bound at prefill shapes).
 //
-// One workgroup = 8 waves = a 256-row x 256-column block of one lane, laid
-// out as 4 (rows) x 2 (columns) waves; each wave owns 64 rows x one
-// 128-column tile, so the per-(row, tile) epilogue results come straight out
-// of one wave.  K advances in 64-row stages through a 2-stage LDS ring filled
-// by direct-to-LDS buffer loads (1 KB per instruction), two 32-deep MFMA steps
-// per stage:
-//   * X stage [256 rows][64 k] bf16, 16-byte units XOR-swizzled by row so
+// One workgroup = 8 waves = a BM-row x 256-column block of one lane (BM =
+// 256, or 128 for 65-128 rows), laid out as 4 (rows) x 2 (columns) waves;
+// each wave owns BM / 4 rows x one 128-column tile, so the per-(row, tile)
+// epilogue results come straight out of one wave.  K advances in BK-row
+// stages (64 for 256-row blocks, 32 for 128-row ones) through an LDS ring of
+// 2 or 3 stages filled by direct-to-LDS buffer loads (1 KB per instruction),
+// one 32-deep MFMA step per 32 rows of a stage:
+//   * X stage [BM rows][BK k] bf16, 16-byte units XOR-swizzled by row so
 //     that the 16 lanes reading one k-group of 16 rows hit distinct banks;
-//   * W stage [64 k][256 columns] bf16, row-major as in HBM; a lane reads an
+//   * W stage [BK k][256 columns] bf16, row-major as in HBM; a lane reads an
 //     8 x 8 block (rows 8g..8g+7, columns 8n..8n+7) and transposes it in
 //     registers with v_perm, as in the decode kernel.
 // Each logit is accumulated over ascending K steps in one wave with
 // v_mfma_f32_16x16x32_bf16.  The token / log-prob / full-logit surfaces all
 // use this mainloop for large batches, so they stay bit-identical.
 // ---------------------------------------------------------------------------
-constexpr int kLBM = kLargeRows, kLBN = 256, kLBK = kLargeStepK;
+constexpr int kLBN = 256;
 constexpr int kLWaves = 8, kLThreads = kLWaves * 64;
-constexpr int kLStages = 2;                     // LDS ring depth (X and W stages)
-constexpr int kLStageXBytes = kLBM * kLBK * 2;  // 32 KB at BK = 64
-constexpr int kLStageWBytes = kLBK * kLBN * 2;  // 32 KB at BK = 64
-constexpr int kLLdsBytes = kLStages * (kLStageXBytes + kLStageWBytes);
-constexpr int kLSub = kLBK / 32;          // 32-deep MFMA steps per stage
-constexpr int kLPieces = kLBK * 2 / 16;   // 16-byte pieces per X row in a stage
-constexpr int kLRowsPerInst = 64 / kLPieces;                  // X rows per 1 KB load
-constexpr int kLXInst = kLBM / kLRowsPerInst / kLWaves;       // X loads per wave per stage
-constexpr int kLWInst = kLBK / 2 / kLWaves;                   // W loads per wave per stage
-static_assert(kLBK == 32 || kLBK == 64, "X swizzle is defined for 4 or 8 pieces per row");
-static_assert(kLLdsBytes <= 160 * 1024, "LDS rings must fit in 160 KB");
-static_assert(kLStages == 2, "the wait counts below assume a two-stage ring");
 
-// X stage layout: 1 KB load j holds rows j*R .. j*R+R-1 (R = kLRowsPerInst);
-// the 16-byte piece q of row r sits in slot q ^ swz(r, j).  The swizzle
-// spreads the 16 rows a fragment read touches over distinct LDS banks.
+// Block shape of the large-batch kernel: BM rows (256 or 128) x 256 columns,
+// K stages of BK rows (64 or 32).  Each of the 4 x 2 waves owns BM / 4 rows
+// (BM / 64 row blocks of 16) of one 128-column tile.
+//   * 256 x 64: X and W stages of 32 KB each; two stages fill 128 KB of LDS
+//     (one workgroup per CU).
+//   * 128 x 32: X 8 KB and W 16 KB per stage; three stages take 72 KB, so two
+//     workgroups share a CU, each with two stages of loads in flight while
+//     it computes one.
+template <int BM, int BK>
+struct LargeShape {
+    static_assert((BM == 256 && BK == 64) || (BM == 128 && (BK == 32 || BK == 64)),
+                  "256 x 64, 128 x 64 or 128 x 32 blocks");
+    static constexpr int kStages = BM == 256 ? 2 : 3;
+    static constexpr int kStageXBytes = BM * BK * 2;
+    static constexpr int kStageWBytes = BK * kLBN * 2;
+    static constexpr int kLdsBytes = kStages * (kStageXBytes + kStageWBytes);
+    static constexpr int kSub = BK / 32;             // 32-deep MFMA steps per stage
+    static constexpr int kPieces = BK * 2 / 16;      // 16-byte pieces per X row in a stage
+    static constexpr int kRowsPerInst = 64 / kPieces;  // X rows per 1 KB load
+    static constexpr int kXInst = BM / kRowsPerInst / kLWaves;  // X loads per wave per stage
+    static constexpr int kWInst = BK / 2 / kLWaves;             // W loads per wave per stage
+    static constexpr int kWaveRows = BM / 4;
+    static constexpr int kRB = kWaveRows / kRowBlock;           // row blocks per wave
+    static_assert(kLdsBytes <= 160 * 1024, "LDS rings must fit in 160 KB");
+    static_assert(kXInst + kWInst <= 15, "a stage's loads fit the vmcnt wait below");
+    static_assert(kXInst >= 1 && kWInst >= 1, "every wave loads part of each stage");
+};
+
+// X stage layout: 1 KB load j holds rows j*R .. j*R+R-1 (R = 64 / P rows of
+// P 16-byte pieces); the piece q of row r sits in slot q ^ swz(r, j).  The
+// swizzle spreads the 16 rows a fragment read touches over distinct LDS banks.
+template <int P>
 __device__ __forceinline__ int x_swz(int r, int j)
 {
-    return kLPieces == 4 ? ((r >> 2) & 3) : (((r >> 1) & 3) | ((j & 1) << 2));
+    static_assert(P == 4 || P == 8, "X swizzle is defined for 4 or 8 pieces per row");
+    return P == 4 ? ((r >> 2) & 3) : (((r >> 1) & 3) | ((j & 1) << 2));
 }
 
 struct LargeGrid {
-    int mblocks;  // ceil(B / 256)
+    int mblocks;  // ceil(B / block rows)
     int sm;       // m-blocks per super-tile (8, 4 or 2), or 0 for the plain order
     int nblocks;  // total 256-column blocks over all lanes
 };
@@ -1156,10 +960,49 @@ __device__ __forceinline__ int nblock_lane(const HeadArgs &a, int nb, int &nb0)
     return lane;
 }
 
-template <int EPI>
+// One K step's direct-to-LDS loads of a large-batch block: this wave's XI
+// 1 KB loads of hidden rows (k0 = st * BK on) into xst and its WI loads of
+// weight rows into wst, through buffer resources rebased at the step so that
+// the 32-bit offsets stay within one stage.
+template <int XI, int WI, int BK>
+__device__ __forceinline__ void large_stage_loads(uint8_t *xst, uint8_t *wst, const uint16_t *xbase,
+                                                  int64_t xbytes, const uint16_t *wbase,
+                                                  int64_t wbytes, int st, int64_t ldw,
+                                                  const uint32_t *xvo, const uint32_t *wvo,
+                                                  int wave)
+{
+    const int k0 = st * BK;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + k0, xbytes - (int64_t)k0 * 2);
+#pragma unroll
+    for (int i = 0; i < XI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (__attribute__((address_space(3))) void *)(xst + (XI * wave + i) * 1024), 16,
+            xvo[i], 0, 0, 0);
+    const int64_t wshift = (int64_t)st * BK * ldw;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + wshift, wbytes - wshift * 2);
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rw, (__attribute__((address_space(3))) void *)(wst + (WI * wave + i) * 1024), 16,
+            wvo[i], 0, 0, 0);
+}
+
+template <int EPI, int BM, int BK>
 __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const HeadArgs a,
                                                                        const LargeGrid grid)
 {
+    // the block shape as local constants (usable in device code as values)
+    using Shape = LargeShape<BM, BK>;
+    constexpr int kStages = Shape::kStages;
+    constexpr int kStageXBytes = Shape::kStageXBytes;
+    constexpr int kStageWBytes = Shape::kStageWBytes;
+    constexpr int kSub = Shape::kSub;
+    constexpr int kPieces = Shape::kPieces;
+    constexpr int kRowsPerInst = Shape::kRowsPerInst;
+    constexpr int kXInst = Shape::kXInst;
+    constexpr int kWInst = Shape::kWInst;
+    constexpr int kWaveRows = Shape::kWaveRows;
+    constexpr int RB = Shape::kRB;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     int mb, nb;
     if (!large_block(grid, blockIdx.x, mb, nb))
@@ -1171,7 +1014,7 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     // lane's first block) and the first column loaded
     const int c0 = (nb - nb0) * kLBN - a.lanes.shift[lane];
     const int cb = max(c0, 0);
-    const int m0 = mb * kLBM;
+    const int m0 = mb * BM;
     const int H = a.H;
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1182,88 +1025,78 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     const uint16_t *wbase = a.lanes.w[lane] + cb;
     const int64_t wcols = ((int64_t)(Vi - cb) + 7) & ~(int64_t)7;
     const int64_t wbytes = H > 0 ? (((int64_t)(H - 1) * a.ldw) + wcols) * 2 : 0;
-    const int rows_here = min(a.B - m0, kLBM);
+    const int rows_here = min(a.B - m0, BM);
     const uint16_t *xbase = a.x + (int64_t)m0 * a.ldx;
     const int64_t xbytes = H > 0 ? (((int64_t)(rows_here - 1) * a.ldx) + ((H + 7) & ~7)) * 2 : 0;
 
-    // this wave's loads per stage: X loads kLXInst*wave .. (kLRowsPerInst rows
-    // each) and W loads kLWInst*wave .. (2 rows of 512 B each)
-    uint32_t xvo[kLXInst], wvo[kLWInst];
+    // this wave's loads per stage: X loads kXInst*wave .. (kRowsPerInst rows
+    // each) and W loads kWInst*wave .. (2 rows of 512 B each)
+    uint32_t xvo[kXInst], wvo[kWInst];
 #pragma unroll
-    for (int i = 0; i < kLXInst; ++i) {
-        const int j = kLXInst * wave + i;
-        const int r = L / kLPieces;
-        const int q = (L % kLPieces) ^ x_swz(r, j);
-        xvo[i] = (uint32_t)((((int64_t)(kLRowsPerInst * j + r)) * a.ldx + 8 * q) * 2);
+    for (int i = 0; i < kXInst; ++i) {
+        const int j = kXInst * wave + i;
+        const int r = L / kPieces;
+        const int q = (L % kPieces) ^ x_swz<kPieces>(r, j);
+        xvo[i] = (uint32_t)((((int64_t)(kRowsPerInst * j + r)) * a.ldx + 8 * q) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < kLWInst; ++i) {
-        const int j = kLWInst * wave + i;
+    for (int i = 0; i < kWInst; ++i) {
+        const int j = kWInst * wave + i;
         const int wrow = 2 * j + (L >> 5);
         wvo[i] = (uint32_t)((((int64_t)wrow) * a.ldw + max(c0 + 8 * (L & 31) - cb, 0)) * 2);
     }
-    const int nsteps = (H + kLBK - 1) / kLBK;
+    const int nsteps = (H + BK - 1) / BK;
     uint8_t *const xring = smem;
-    uint8_t *const wring = smem + kLStages * kLStageXBytes;
-    auto issue_x = [&](int st) {
-        uint8_t *stage = xring + (st % kLStages) * kLStageXBytes;
-        const int k0 = st * kLBK;
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(xbase + k0, xbytes - (int64_t)k0 * 2);
-#pragma unroll
-        for (int i = 0; i < kLXInst; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (__attribute__((address_space(3))) void *)(stage + (kLXInst * wave + i) * 1024),
-                16, xvo[i], 0, 0, 0);
-    };
-    auto issue_w = [&](int st) {
-        uint8_t *stage = wring + (st % kLStages) * kLStageWBytes;
-        const int64_t wshift = (int64_t)st * kLBK * a.ldw;
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase + wshift, wbytes - wshift * 2);
-#pragma unroll
-        for (int i = 0; i < kLWInst; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (__attribute__((address_space(3))) void *)(stage + (kLWInst * wave + i) * 1024),
-                16, wvo[i], 0, 0, 0);
-    };
+    uint8_t *const wring = smem + kStages * kStageXBytes;
 
-    f32x4 acc[4][8];
+    f32x4 acc[RB][8];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int c = 0; c < 8; ++c)
             acc[rb][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Two-stage ring: step st+1 is loaded while step st is computed.
-    if (nsteps > 0) {
-        issue_x(0);
-        issue_w(0);
-    }
+    // A ring of kStages stages: the loads of steps st+1 .. st+kStages-1 are
+    // in flight while step st is computed.
+#pragma unroll
+    for (int p = 0; p < kStages - 1; ++p)
+        if (p < nsteps)
+            large_stage_loads<kXInst, kWInst, BK>(xring + p * kStageXBytes, wring + p * kStageWBytes, xbase,
+                                      xbytes, wbase, wbytes, p, a.ldw, xvo, wvo, wave);
     for (int st = 0; st < nsteps; ++st) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of step st
-        __builtin_amdgcn_s_barrier();        // every wave's loads are in LDS and
-                                             // every wave is done reading step st-1
-        if (st + 1 < nsteps) {
-            issue_x(st + 1);                 // refills the slots of step st-1
-            issue_w(st + 1);
+        // This wave's loads of step st are done.  Loads complete in order, so
+        // with three stages the kXInst + kWInst loads of step st+1, issued
+        // later, may still be in flight.
+        if (kStages == 3 && st + 1 < nsteps)
+            __builtin_amdgcn_s_waitcnt(0x0f70 | (kXInst + kWInst));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+        __builtin_amdgcn_s_barrier();  // every wave's loads of step st are in LDS and
+                                       // every wave is done reading step st-1
+        if (st + kStages - 1 < nsteps) {
+            // refills the slots of step st-1
+            const int sn = st + kStages - 1, slot = sn % kStages;
+            large_stage_loads<kXInst, kWInst, BK>(xring + slot * kStageXBytes, wring + slot * kStageWBytes,
+                                      xbase, xbytes, wbase, wbytes, sn, a.ldw, xvo, wvo, wave);
         }
-        const uint8_t *stage = xring + (st % kLStages) * kLStageXBytes;
-        const uint8_t *wst = wring + (st % kLStages) * kLStageWBytes;
+        const uint8_t *stage = xring + (st % kStages) * kStageXBytes;
+        const uint8_t *wst = wring + (st % kStages) * kStageWBytes;
 #pragma unroll
-        for (int ks = 0; ks < kLSub; ++ks) {
-            const int k0 = st * kLBK + 32 * ks;
-            u32x4 af[4];
+        for (int ks = 0; ks < kSub; ++ks) {
+            const int k0 = st * BK + 32 * ks;
+            u32x4 af[RB];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int row = wr * 64 + rb * 16 + n;
-                const int j = row / kLRowsPerInst, r = row % kLRowsPerInst;
+            for (int rb = 0; rb < RB; ++rb) {
+                const int row = wr * kWaveRows + rb * 16 + n;
+                const int j = row / kRowsPerInst, r = row % kRowsPerInst;
                 const int piece = 4 * ks + g;
                 af[rb] = *reinterpret_cast<const u32x4 *>(
-                    stage + j * 1024 + (r * kLPieces + (piece ^ x_swz(r, j))) * 16);
+                    stage + j * 1024 + (r * kPieces + (piece ^ x_swz<kPieces>(r, j))) * 16);
             }
             if (k0 + 32 > H) {
                 const int h0 = k0 + 8 * g;
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
                         uint32_t v = af[rb][d];
@@ -1279,9 +1112,9 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
             for (int r = 0; r < 8; ++r)
                 wq[r] = *reinterpret_cast<const u32x4 *>(wst + (32 * ks + 8 * g + r) * (kLBN * 2) +
                                                          (wc * 128 + 8 * n) * 2);
-            bf16x8 xa[4];
+            bf16x8 xa[RB];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
+            for (int rb = 0; rb < RB; ++rb)
                 xa[rb] = __builtin_bit_cast(bf16x8, af[rb]);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
@@ -1292,7 +1125,7 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
                     bq[q] = __builtin_amdgcn_perm(wq[2 * q + 1][c >> 1], wq[2 * q][c >> 1], sel);
                 const bf16x8 bb = __builtin_bit_cast(bf16x8, bq);
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
+                for (int rb = 0; rb < RB; ++rb)
                     acc[rb][c] =
                         __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[rb], bb, acc[rb][c], 0, 0, 0);
             }
@@ -1308,10 +1141,10 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     const int nvalid = colrel < 0 ? 0 : max(0, min(8, Vi - colrel));
     const int gcol = a.lanes.off[lane] + colrel;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int b = m0 + wr * 64 + rb * 16 + 4 * g + r;
+            const int b = m0 + wr * kWaveRows + rb * 16 + 4 * g + r;
             const bool rowok = b < a.B;
             float y[8];
 #pragma unroll
@@ -1368,11 +1201,11 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     }
 }
 
-template <int EPI>
+template <int EPI, int BM, int BK>
 hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
 {
     LargeGrid g;
-    g.mblocks = (a.B + kLBM - 1) / kLBM;
+    g.mblocks = (a.B + BM - 1) / BM;
     g.nblocks = 0;
     for (int i = 0; i < a.lanes.k; ++i)
         g.nblocks += (a.lanes.off[i + 1] - a.lanes.off[i] + a.lanes.shift[i] + kLBN - 1) / kLBN;
@@ -1386,14 +1219,22 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
     } else {
         nwg = (int64_t)g.mblocks * g.nblocks;
     }
-    const size_t lds = (size_t)kLLdsBytes;
+    const size_t lds = (size_t)LargeShape<BM, BK>::kLdsBytes;
     static std::atomic<uint64_t> lds_done{0};
-    const hipError_t e = raise_lds_limit((const void *)head_gemm_large_kernel<EPI>, (int)lds, lds_done);
+    const hipError_t e =
+        raise_lds_limit((const void *)head_gemm_large_kernel<EPI, BM, BK>, (int)lds, lds_done);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(head_gemm_large_kernel<EPI>, dim3((unsigned)nwg), dim3(kLThreads), lds, s,
-                       a, g);
+    hipLaunchKernelGGL((head_gemm_large_kernel<EPI, BM, BK>), dim3((unsigned)nwg),
+                       dim3(kLThreads), lds, s, a, g);
     return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_large_rows(const HeadArgs &a, hipStream_t s)
+{
+    return large_block_rows(a.B) == 128 ? launch_large_epi<EPI, 128, kLargeSmallStepK>(a, s)
+                                        : launch_large_epi<EPI, 256, kLargeStepK>(a, s);
 }
 
 template <int MB, int POL, bool XP = false>
@@ -1660,11 +1501,10 @@ hipError_t launch_head_gemm(const HeadArgs &a, int epi, hipStream_t s)
     case 2:
         return launch_mb<2, kPolicyStream>(a, epi, s);
     default:
-        // One row group streams each weight tile once; with several row
-        // groups two tiles per workgroup share the hidden rows.
-        if (a.B <= kRowBlock * kMaxMB)
-            return launch_mb<kMaxMB, kPolicyStream, true>(a, epi, s);
-        return launch_pair<kPolicyShared>(a, epi, s);
+        // more than one row group is the large-batch kernel's
+        if (a.B > kRowBlock * kMaxMB)
+            return hipErrorInvalidValue;
+        return launch_mb<kMaxMB, kPolicyStream, true>(a, epi, s);
     }
 }
 
@@ -1674,13 +1514,13 @@ hipError_t launch_head_gemm_large(const HeadArgs &a, int epi, hipStream_t s)
         return hipSuccess;
     switch (epi) {
     case kEpiPair:
-        return launch_large_epi<kEpiPair>(a, s);
+        return launch_large_rows<kEpiPair>(a, s);
     case kEpiPairLse:
-        return launch_large_epi<kEpiPairLse>(a, s);
+        return launch_large_rows<kEpiPairLse>(a, s);
     case kEpiPairLseOut:
-        return launch_large_epi<kEpiPairLseOut>(a, s);
+        return launch_large_rows<kEpiPairLseOut>(a, s);
     case kEpiShard:
-        return launch_large_epi<kEpiShard>(a, s);
+        return launch_large_rows<kEpiShard>(a, s);
     default:
         return hipErrorInvalidValue;
     }

@@ -66,15 +66,15 @@ sb_status check_desc(const sb_head_desc *d)
         return SB_ERR_UNSUPPORTED;
     // Per-step buffer offsets are 32-bit: 40 hidden rows of a shard and one
     // row group of x must span less than 4 GiB; for the large-batch kernel
-    // (B >= 129) a K stage of a shard (64 rows, plus 8) and a 256-row block
-    // of x.
+    // (B >= 65) a K stage of a shard (32 rows up to 128 rows, else 64; plus 8)
+    // and one block of x (128 rows up to 128 rows, else 256).
     const int64_t lim = (int64_t)1 << 32;
     if ((int64_t)(sbk::kStepK + 8) * d->ldw * 2 >= lim ||
         (int64_t)(sbk::kRowBlock * sbk::kMaxMB) * d->ldx * 2 >= lim)
         return SB_ERR_UNSUPPORTED;
     if (d->B >= sbk::kLargeBatch &&
-        ((int64_t)(sbk::kLargeStepK + 8) * d->ldw * 2 >= lim ||
-         (int64_t)sbk::kLargeRows * d->ldx * 2 >= lim))
+        ((int64_t)(sbk::large_step_k(d->B) + 8) * d->ldw * 2 >= lim ||
+         (int64_t)sbk::large_block_rows(d->B) * d->ldx * 2 >= lim))
         return SB_ERR_UNSUPPORTED;
     return SB_OK;
 }

@@ -178,21 +178,34 @@ def test_descriptor_validation(kw, status):
 
 
 def test_large_batch_offset_limits():
-    """From 129 rows the large-batch kernel's 32-bit buffer offsets span a
-    256-row block of x and a 64-row K stage of a shard (plus 8 rows of
-    slack): validation rejects strides where those reach 4 GiB, and accepts
-    them below 129 rows, where the decode kernels reach 64 rows of x and 40
-    rows of a shard."""
-    ldx = 1 << 23                   # 256 rows x 2 B = 4 GiB
+    """The kernels' 32-bit buffer offsets: up to 64 rows the decode kernels
+    reach 64 rows of x and 40 rows of a shard; from 65 to 128 rows the
+    large-batch kernel's 128-row blocks reach 128 rows of x and 32-row K
+    stages (plus 8 rows of slack: 40 shard rows); from 129 rows its 256-row
+    blocks reach 256 rows of x and 64-row K stages (72 shard rows).
+    Validation rejects strides where those reach 4 GiB and accepts them just
+    below."""
+    lim = 1 << 32
+    ldx256 = 1 << 23                # 256 rows x 2 B = 4 GiB
+    ldx128 = 1 << 24                # 128 rows x 2 B = 4 GiB
     ldw = 29826168                  # 72 rows x 2 B >= 4 GiB > 40 rows x 2 B
-    assert (256 * ldx * 2 >= 1 << 32) and (72 * ldw * 2 >= 1 << 32) and (40 * ldw * 2 < 1 << 32)
-    assert ws_status(fake_head(B=129, ldx=ldx)) == sb.SB_ERR_UNSUPPORTED
-    assert ws_status(fake_head(B=128, ldx=ldx)) == sb.SB_OK
-    assert ws_status(fake_head(B=129, ldx=ldx - 8)) == sb.SB_OK
+    assert 256 * ldx256 * 2 >= lim and 128 * ldx128 * 2 >= lim and 64 * (ldx128 - 8) * 2 < lim
+    assert 72 * ldw * 2 >= lim and 40 * ldw * 2 < lim
+    # x: 256-row blocks from 129 rows, 128-row blocks from 65 to 128 rows
+    assert ws_status(fake_head(B=129, ldx=ldx256)) == sb.SB_ERR_UNSUPPORTED
+    assert ws_status(fake_head(B=129, ldx=ldx256 - 8)) == sb.SB_OK
+    assert ws_status(fake_head(B=128, ldx=ldx256)) == sb.SB_OK
+    assert ws_status(fake_head(B=128, ldx=ldx128)) == sb.SB_ERR_UNSUPPORTED
+    assert ws_status(fake_head(B=65, ldx=ldx128)) == sb.SB_ERR_UNSUPPORTED
+    assert ws_status(fake_head(B=65, ldx=ldx128 - 8)) == sb.SB_OK
+    assert ws_status(fake_head(B=64, ldx=ldx128 - 8)) == sb.SB_OK
+    # shard rows: 72 from 129 rows, 40 below
     assert ws_status(fake_head(B=129, ldw=ldw)) == sb.SB_ERR_UNSUPPORTED
     assert ws_status(fake_head(B=128, ldw=ldw)) == sb.SB_OK
+    assert ws_status(fake_head(B=65, ldw=ldw)) == sb.SB_OK
     assert ws_status(fake_head(B=2048, ldw=ldw - 8)) == sb.SB_OK
-    assert tokens_status(fake_head(B=129, ldx=ldx)) == sb.SB_ERR_UNSUPPORTED
+    assert tokens_status(fake_head(B=129, ldx=ldx256)) == sb.SB_ERR_UNSUPPORTED
+    assert tokens_status(fake_head(B=100, ldx=ldx128)) == sb.SB_ERR_UNSUPPORTED
     assert tokens_status(fake_head(B=300, ldw=ldw)) == sb.SB_ERR_UNSUPPORTED
 
 

@@ -31,7 +31,7 @@ CASES = [
     (20, 640, 9001, [0, 3000, 3001, 9001], True),          # two row blocks, ragged
     (48, 1024, 30000, inputs.equal_lanes(30000, 7), True),  # packed hidden rows
     (16, 4160, 37984, [0, 37984], False),                   # two K slices
-    (100, 512, 20000, [0, 7, 19000, 20000], True),          # two-tile kernel
+    (100, 512, 20000, [0, 7, 19000, 20000], True),          # 128-row blocks
     (300, 136, 6000, [0, 2500, 2501, 6000], True),          # large-batch kernel
     (129, 64, 2050, inputs.equal_lanes(2050, 50), True),    # large-batch, 50 lanes
 ]

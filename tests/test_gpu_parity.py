@@ -120,7 +120,7 @@ def test_maximum_lane_count(require_gpu, B, sep):
     (3, 64, 1, [0, 1]),              # a single vocabulary column
     (5, 32, 8, list(range(9))),      # eight lanes of one column each
     (40, 1, 300, [0, 100, 300]),     # H = 1: one product per logit
-    (70, 1, 300, [0, 100, 300]),     # ... with two tiles per workgroup
+    (70, 1, 300, [0, 100, 300]),     # ... with 128-row large-batch blocks
 ])
 def test_degenerate_heads(require_gpu, B, H, V, off):
     """Smallest vocabularies, one-column lanes and a one-element hidden size

@@ -128,7 +128,7 @@ def test_one_workspace_for_every_shape_surface_and_entry_point(require_gpu):
     calls = [
         ("tokens", 3, 256, 1000, 1),
         ("full", 40, 512, 6000, 8),
-        ("logprobs", 128, 512, 3000, 5),  # two row groups of the pair kernel
+        ("logprobs", 128, 512, 3000, 5),  # one 128-row large-batch block
         ("tokens", 64, 2048, 3000, 16),   # split, 16 lanes
         ("logprobs", 20, 640, 9000, 3),
         ("partial", 16, 0, 520, 2),

@@ -21,8 +21,8 @@ from tests.gpu_common import check_against_oracle, upload
 pytestmark = pytest.mark.gpu
 
 # One head per dispatch path: one, two and four 16-row blocks (the last with
-# the packed hidden rows), split heads (8 and 2 K slices), the two-tile
-# kernel over two row groups, and the large-batch kernel.
+# the packed hidden rows), split heads (8 and 2 K slices), and the
+# large-batch kernel with 128-row (B = 100) and 256-row (B = 200) blocks.
 HEADS = [
     # B, H, V, k
     (5, 512, 20000, 3),

@@ -30,7 +30,7 @@ def _both(d):
     # (B, H, V, k): a larger call, then a smaller one on the same array
     ((64, 4096, 50000, 4), (5, 512, 9000, 2)),       # packed rows, then one row block
     ((16, 4160, 37984, 1), (3, 256, 1000, 3)),       # two K slices, then a small head
-    ((300, 512, 20000, 3), (100, 256, 8000, 2)),     # large-batch kernel, then two tiles
+    ((300, 512, 20000, 3), (100, 256, 8000, 2)),     # 256-row, then 128-row blocks
 ])
 def test_static_scratch_matches_the_workspace_call(require_gpu, first, second):
     for i, (B, H, V, k) in enumerate((first, second)):
