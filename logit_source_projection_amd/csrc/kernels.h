@@ -171,7 +171,9 @@ constexpr int kLargeBatch = 65;
 constexpr int kLargeRows = 256;
 constexpr int kLargeSmallMax = 128;
 constexpr int kLargeStepK = 64;
+constexpr int kLargeStages = 2;
 constexpr int kLargeSmallStepK = 32;
+constexpr int kLargeSmallStages = 3;
 inline int large_block_rows(int B) { return B <= kLargeSmallMax ? 128 : kLargeRows; }
 inline int large_step_k(int B) { return B <= kLargeSmallMax ? kLargeSmallStepK : kLargeStepK; }
 

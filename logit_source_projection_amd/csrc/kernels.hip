@@ -864,18 +864,18 @@ constexpr int kLBN = 256;
 constexpr int kLWaves = 8, kLThreads = kLWaves * 64;
 
 // Block shape of the large-batch kernel: BM rows (256 or 128) x 256 columns,
-// K stages of BK rows (64 or 32).  Each of the 4 x 2 waves owns BM / 4 rows
-// (BM / 64 row blocks of 16) of one 128-column tile.
-//   * 256 x 64: X and W stages of 32 KB each; two stages fill 128 KB of LDS
+// K stages of BK rows (64 or 32) in a ring of ST stages.  Each of the 4 x 2
+// waves owns BM / 4 rows (BM / 64 row blocks of 16) of one 128-column tile.
+//   * 256 x 64, 2 stages: X and W stages of 32 KB each fill 128 KB of LDS
 //     (one workgroup per CU).
-//   * 128 x 32: X 8 KB and W 16 KB per stage; three stages take 72 KB, so two
+//   * 128 x 32, 3 stages: X 8 KB and W 16 KB per stage take 72 KB, so two
 //     workgroups share a CU, each with two stages of loads in flight while
 //     it computes one.
-template <int BM, int BK>
+template <int BM, int BK, int ST>
 struct LargeShape {
-    static_assert((BM == 256 && BK == 64) || (BM == 128 && (BK == 32 || BK == 64)),
-                  "256 x 64, 128 x 64 or 128 x 32 blocks");
-    static constexpr int kStages = BM == 256 ? 2 : 3;
+    static_assert((BM == 256 || BM == 128) && (BK == 64 || BK == 32) && ST >= 2,
+                  "256- or 128-row blocks, 64- or 32-deep stages, two or more of them");
+    static constexpr int kStages = ST;
     static constexpr int kStageXBytes = BM * BK * 2;
     static constexpr int kStageWBytes = BK * kLBN * 2;
     static constexpr int kLdsBytes = kStages * (kStageXBytes + kStageWBytes);
@@ -887,7 +887,7 @@ struct LargeShape {
     static constexpr int kWaveRows = BM / 4;
     static constexpr int kRB = kWaveRows / kRowBlock;           // row blocks per wave
     static_assert(kLdsBytes <= 160 * 1024, "LDS rings must fit in 160 KB");
-    static_assert(kXInst + kWInst <= 15, "a stage's loads fit the vmcnt wait below");
+    static_assert((ST - 1) * (kXInst + kWInst) <= 15, "the later stages' loads fit a vmcnt wait");
     static_assert(kXInst >= 1 && kWInst >= 1, "every wave loads part of each stage");
 };
 
@@ -987,12 +987,12 @@ __device__ __forceinline__ void large_stage_loads(uint8_t *xst, uint8_t *wst, co
             wvo[i], 0, 0, 0);
 }
 
-template <int EPI, int BM, int BK>
+template <int EPI, int BM, int BK, int ST>
 __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const HeadArgs a,
                                                                        const LargeGrid grid)
 {
     // the block shape as local constants (usable in device code as values)
-    using Shape = LargeShape<BM, BK>;
+    using Shape = LargeShape<BM, BK, ST>;
     constexpr int kStages = Shape::kStages;
     constexpr int kStageXBytes = Shape::kStageXBytes;
     constexpr int kStageWBytes = Shape::kStageWBytes;
@@ -1065,10 +1065,14 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
                                       xbytes, wbase, wbytes, p, a.ldw, xvo, wvo, wave);
     for (int st = 0; st < nsteps; ++st) {
         // This wave's loads of step st are done.  Loads complete in order, so
-        // with three stages the kXInst + kWInst loads of step st+1, issued
-        // later, may still be in flight.
-        if (kStages == 3 && st + 1 < nsteps)
-            __builtin_amdgcn_s_waitcnt(0x0f70 | (kXInst + kWInst));
+        // the kXInst + kWInst loads of each of the up to kStages - 2 later
+        // steps issued so far may still be in flight.
+        constexpr int kLoads = kXInst + kWInst;
+        const int later = min(kStages - 2, nsteps - 1 - st);
+        if (kStages >= 4 && later >= 2)
+            __builtin_amdgcn_s_waitcnt(0x0f70 | (kStages >= 4 ? 2 * kLoads : 0));
+        else if (kStages >= 3 && later >= 1)
+            __builtin_amdgcn_s_waitcnt(0x0f70 | (kStages >= 3 ? kLoads : 0));
         else
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __builtin_amdgcn_s_barrier();  // every wave's loads of step st are in LDS and
@@ -1201,7 +1205,7 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     }
 }
 
-template <int EPI, int BM, int BK>
+template <int EPI, int BM, int BK, int ST>
 hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
 {
     LargeGrid g;
@@ -1219,13 +1223,13 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
     } else {
         nwg = (int64_t)g.mblocks * g.nblocks;
     }
-    const size_t lds = (size_t)LargeShape<BM, BK>::kLdsBytes;
+    const size_t lds = (size_t)LargeShape<BM, BK, ST>::kLdsBytes;
     static std::atomic<uint64_t> lds_done{0};
     const hipError_t e =
-        raise_lds_limit((const void *)head_gemm_large_kernel<EPI, BM, BK>, (int)lds, lds_done);
+        raise_lds_limit((const void *)head_gemm_large_kernel<EPI, BM, BK, ST>, (int)lds, lds_done);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((head_gemm_large_kernel<EPI, BM, BK>), dim3((unsigned)nwg),
+    hipLaunchKernelGGL((head_gemm_large_kernel<EPI, BM, BK, ST>), dim3((unsigned)nwg),
                        dim3(kLThreads), lds, s, a, g);
     return hipGetLastError();
 }
@@ -1233,8 +1237,9 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
 template <int EPI>
 hipError_t launch_large_rows(const HeadArgs &a, hipStream_t s)
 {
-    return large_block_rows(a.B) == 128 ? launch_large_epi<EPI, 128, kLargeSmallStepK>(a, s)
-                                        : launch_large_epi<EPI, 256, kLargeStepK>(a, s);
+    return large_block_rows(a.B) == 128
+               ? launch_large_epi<EPI, 128, kLargeSmallStepK, kLargeSmallStages>(a, s)
+               : launch_large_epi<EPI, 256, kLargeStepK, kLargeStages>(a, s);
 }
 
 template <int MB, int POL, bool XP = false>
