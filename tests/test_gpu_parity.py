@@ -121,6 +121,9 @@ def test_maximum_lane_count(require_gpu, B, sep):
     (5, 32, 8, list(range(9))),      # eight lanes of one column each
     (40, 1, 300, [0, 100, 300]),     # H = 1: one product per logit
     (70, 1, 300, [0, 100, 300]),     # ... with 128-row large-batch blocks
+    (200, 1, 300, [0, 100, 300]),    # ... with 256-row large-batch blocks
+    (300, 64, 1, [0, 1]),            # one column, two 256-row blocks
+    (100, 40, 9, [0, 1, 2, 9]),      # one-column lanes in 128-row blocks
 ])
 def test_degenerate_heads(require_gpu, B, H, V, off):
     """Smallest vocabularies, one-column lanes and a one-element hidden size
