@@ -493,8 +493,9 @@ def main():
     # HIP events bracket the whole call, so `achieved` is the call's rate: a
     # lower bound on the head kernel's own rate (the combine launch that
     # follows it is a few microseconds; rocprofv3 gives both kernels apart).
-    if B <= 128 and args.surface in ("tokens", "logprobs"):
-        kernel = ("whole call: head_gemm_kernel + combine_kernel"
+    if args.surface in ("tokens", "logprobs"):
+        head = "head_gemm_kernel" if B <= 64 else "head_gemm_large_kernel"
+        kernel = (f"whole call: {head} + combine_kernel"
                   + (" (after the hidden-row pack)" if 32 < B <= 64 else ""))
     else:
         kernel = "whole call (head GEMM and its follow-up kernels)"
