@@ -39,9 +39,10 @@
  *
  * Ownership and threading
  *  - The caller allocates every device buffer.  The library allocates no
- *    device memory and is thread-safe.  The only thing it keeps between
- *    calls is a per-device note that it has raised two kernels' LDS limits
- *    (hipFuncSetAttribute, once per device).
+ *    device memory and is thread-safe.  The only things it keeps between
+ *    calls are a per-device note of the kernels whose LDS limit it has
+ *    raised (hipFuncSetAttribute, once per device and kernel) and, for
+ *    sb_project_tokens_static, each device's address of its static array.
  *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
  *    the default stream).  Inputs are read-only.
  *  - The workspace is scratch owned by the call until its work completes on

@@ -1,7 +1,7 @@
 """GPU test of the library's thread safety: several host threads call it at
 once, each on its own stream with its own workspace and outputs, on heads of
 different dispatch paths.  The library keeps no state between calls beyond a
-per-device note that it has raised two kernels' LDS limits, so every result
+per-device note of the kernels whose LDS limit it has raised, so every result
 must equal the same call made alone, bit for bit."""
 import threading
 
