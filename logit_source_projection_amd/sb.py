@@ -114,6 +114,44 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# Argument checks of the binding: a host tensor, a wrong dtype or a strided
+# layout the C ABI cannot express would otherwise reach a kernel as a raw
+# pointer.  They raise before anything is enqueued.
+def _device(t, name, dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+
+
+def _vector(t, name, dtype, n):
+    """A contiguous device buffer of at least n elements (None allowed)."""
+    if t is None:
+        return
+    _device(t, name, dtype)
+    if not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name} must be contiguous with at least {n} elements")
+
+
+def _matrix(t, name, dtype, rows, cols):
+    """A [>= rows, >= cols] device matrix with unit column stride (None allowed)."""
+    if t is None:
+        return
+    _device(t, name, dtype)
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < cols or (
+            t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a [>= {rows}, >= {cols}] matrix with unit column stride")
+
+
+def _operands(tensors, name):
+    """The bf16 operands a descriptor was built from: on the device, rows
+    with unit column stride."""
+    for t in tensors:
+        _device(t, name, torch.bfloat16)
+        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError(f"{name} must be 2-D with unit column stride")
+
+
 def _stream(stream):
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -136,6 +174,8 @@ class Head:
                  ldw=None, x_ptr=None, w_ptrs=None):
         self.x = x
         self.w = w
+        # built from tensors (checked on every call) or from raw pointers
+        self.from_tensors = x_ptr is None and w_ptrs is None
         off = [int(o) for o in lane_off]
         self.lane_off = off
         k = len(off) - 1
@@ -171,6 +211,11 @@ class Head:
 
     def ref(self):
         return ctypes.byref(self.desc)
+
+    def check(self):
+        if self.from_tensors:
+            _operands([self.x], "x")
+            _operands(self.w if isinstance(self.w, (list, tuple)) else [self.w], "w")
 
 
 def sb_workspace_bytes(head, surface):
@@ -216,6 +261,9 @@ def _check(status, where):
 
 def sb_project_tokens(head, ids, ws=None, stream=None):
     """Token-only surface: ids (int32 [B], device) <- argmax token IDs."""
+    head.check()
+    _vector(ids, "ids", torch.int32, head.B)
+    _vector(ws, "ws", torch.uint8, 0)
     ws = _workspace(lambda: sb_workspace_bytes(head, SB_SURF_TOKENS), ws, ids.device, stream)
     _check(lib().sb_project_tokens(head.ref(), _ptr(ids), _ptr(ws), ws.numel(),
                                    _stream(stream)), "sb_project_tokens")
@@ -225,6 +273,8 @@ def sb_project_tokens(head, ids, ws=None, stream=None):
 def sb_project_tokens_static(head, ids, stream=None):
     """Token-only surface with the library's static device scratch as the
     workspace (no allocation; SB_STATIC_SCRATCH_BYTES at most)."""
+    head.check()
+    _vector(ids, "ids", torch.int32, head.B)
     _check(lib().sb_project_tokens_static(head.ref(), _ptr(ids), _stream(stream)),
            "sb_project_tokens_static")
     return ids
@@ -236,6 +286,12 @@ SB_STATIC_SCRATCH_BYTES = 32 << 20
 def sb_project_lane_results(head, ids, lane_ids=None, lane_max=None, ws=None, stream=None):
     """Token surface plus each lane's own result: lane_ids (int32 [B, k]) and
     lane_max (fp32 [B, k]) of every row, either optional."""
+    head.check()
+    k = head.desc.k
+    _vector(ids, "ids", torch.int32, head.B)
+    _vector(lane_ids, "lane_ids", torch.int32, head.B * k)
+    _vector(lane_max, "lane_max", torch.float32, head.B * k)
+    _vector(ws, "ws", torch.uint8, 0)
     ws = _workspace(lambda: sb_workspace_bytes(head, SB_SURF_TOKENS), ws, ids.device, stream)
     _check(lib().sb_project_lane_results(head.ref(), _ptr(ids), _ptr(lane_ids), _ptr(lane_max),
                                          _ptr(ws), ws.numel(), _stream(stream)),
@@ -247,6 +303,12 @@ def sb_project_logprobs(head, ids, lse, sel_lp=None, logprobs=None, ws=None,
                         stream=None):
     """Log-probability surface: ids, lse, optional sel_lp and complete
     fp32 log-probs [B, V] (row stride logprobs.stride(0))."""
+    head.check()
+    _vector(ids, "ids", torch.int32, head.B)
+    _vector(lse, "lse", torch.float32, head.B)
+    _vector(sel_lp, "sel_lp", torch.float32, head.B)
+    _matrix(logprobs, "logprobs", torch.float32, head.B, head.V)
+    _vector(ws, "ws", torch.uint8, 0)
     surf = SB_SURF_LOGPROBS_FULL if logprobs is not None else SB_SURF_LOGPROBS
     ws = _workspace(lambda: sb_workspace_bytes(head, surf), ws, ids.device, stream)
     ld = logprobs.stride(0) if logprobs is not None else 0
@@ -259,6 +321,10 @@ def sb_project_logprobs(head, ids, lse, sel_lp=None, logprobs=None, ws=None,
 def sb_full_logits(head, logits, ids=None, ws=None, stream=None):
     """Full-logit plan: logits fp32 [B, V] (row stride logits.stride(0)),
     optional ids."""
+    head.check()
+    _matrix(logits, "logits", torch.float32, head.B, head.V)
+    _vector(ids, "ids", torch.int32, head.B)
+    _vector(ws, "ws", torch.uint8, 0)
     ws = _workspace(lambda: sb_workspace_bytes(head, SB_SURF_FULL_LOGITS), ws, logits.device,
                     stream)
     _check(lib().sb_full_logits(head.ref(), _ptr(logits), logits.stride(0), _ptr(ids),
@@ -275,6 +341,8 @@ class Partial:
     def __init__(self, x, w, *, B=None, N=None, lane_k=None, ldx=None, ldw=None,
                  x_ptrs=None, w_ptrs=None):
         self.x, self.w = list(x), list(w)
+        # built from tensors (checked on every call) or from raw pointers
+        self.from_tensors = x_ptrs is None and w_ptrs is None
         Ks = [t.shape[1] for t in self.x]
         off = [0]
         for kk in Ks:
@@ -306,6 +374,11 @@ class Partial:
     def ref(self):
         return ctypes.byref(self.desc)
 
+    def check(self):
+        if self.from_tensors:
+            _operands(self.x, "x")
+            _operands(self.w, "w")
+
 
 def sb_partial_workspace_bytes(part):
     st = ctypes.c_int(0)
@@ -320,6 +393,9 @@ def sb_partial_complete(part, op, out, ws=None, stream=None):
     reduction `op` ("sum", "prod", "min", "max" or an SB_RED_* code) of the
     lane partials."""
     code = REDUCE_OPS[op] if isinstance(op, str) else int(op)
+    part.check()
+    _matrix(out, "out", torch.float32, part.B, part.N)
+    _vector(ws, "ws", torch.uint8, 0)
     ws = _workspace(lambda: sb_partial_workspace_bytes(part), ws, out.device, stream)
     _check(lib().sb_partial_complete(part.ref(), code, _ptr(out), out.stride(0), _ptr(ws),
                                      ws.numel(), _stream(stream)), "sb_partial_complete")

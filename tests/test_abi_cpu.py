@@ -384,3 +384,30 @@ def test_header_compiles_as_c99():
         r = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror",
                             "-fsyntax-only", "-I", inc, src], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_binding_refuses_arguments_the_abi_cannot_take():
+    """The Python binding raises, before anything reaches the library, on host
+    tensors and wrong dtypes (which would otherwise reach a kernel as raw
+    pointers).  Without a GPU only each call's first checked argument can be
+    exercised; the GPU tests run every call with valid device arguments."""
+    h = fake_head()                                  # raw device pointers: B=16, V=4096
+    with pytest.raises(ValueError, match="ids must be a device tensor"):
+        sb.sb_project_tokens(h, torch.empty(16, dtype=torch.int32))
+    with pytest.raises(ValueError, match="ids must be a device tensor"):
+        sb.sb_project_tokens_static(h, torch.empty(16, dtype=torch.int64))
+    with pytest.raises(ValueError, match="ids must be a device tensor"):
+        sb.sb_project_lane_results(h, torch.empty(16, dtype=torch.int32))
+    with pytest.raises(ValueError, match="ids must be a device tensor"):
+        sb.sb_project_logprobs(h, torch.empty(16, dtype=torch.int32), torch.empty(16))
+    with pytest.raises(ValueError, match="logits must be a device tensor"):
+        sb.sb_full_logits(h, torch.empty(16, 4096))
+    # a descriptor built from host tensors is refused as a whole
+    host = sb.Head(torch.empty(16, 512, dtype=torch.bfloat16),
+                   torch.empty(512, 4096, dtype=torch.bfloat16), [0, 2048, 4096])
+    with pytest.raises(ValueError, match="x must be a device tensor"):
+        sb.sb_project_tokens(host, None)
+    part = sb.Partial([torch.empty(4, 64, dtype=torch.bfloat16)],
+                      [torch.empty(64, 128, dtype=torch.bfloat16)])
+    with pytest.raises(ValueError, match="x must be a device tensor"):
+        sb.sb_partial_complete(part, "sum", None)
