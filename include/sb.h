@@ -90,10 +90,14 @@ typedef enum sb_status {
                                 a logits / log-probs leading dim not a
                                 multiple of 4                                  */
     SB_ERR_WORKSPACE = -5,   /* workspace smaller than sb_workspace_bytes()   */
-    SB_ERR_UNSUPPORTED = -6, /* B > 65535; or 40 shard rows or 64 rows of x
+    SB_ERR_UNSUPPORTED = -6, /* V > 2^30; or 40 shard rows or 64 rows of x
                                 span 4 GiB or more; or, for 65 <= B <= 128,
-                                128 rows of x do; or, for B >= 129, 72
-                                shard rows or 256 rows of x do             */
+                                128 rows of x
+                                do; or, for B >= 129, 72 shard rows or 256
+                                rows of x do; or a launch of the call would
+                                need 2^32 work items or more in one grid
+                                dimension (B >= 2^24 always does; for
+                                B >= 129 roughly B * V >= 5.5e11)          */
     SB_ERR_HIP = -7          /* a HIP launch failed                            */
 } sb_status;
 
@@ -248,7 +252,10 @@ typedef enum sb_reduce_op {
 } sb_reduce_op;
 
 /*
- *   B       rows (tokens); B == 0 is a valid no-op; B <= 65535
+ *   B       rows (tokens); B == 0 is a valid no-op; the chunked GEMM's
+ *           launch of about ceil(K_i / 1024) * ceil(N / 128) * ceil(B / 64)
+ *           workgroups of 256 work items, summed over lanes, must hold fewer
+ *           than 2^32 work items (else SB_ERR_UNSUPPORTED)
  *   N       output width (the model's hidden size), >= 1
  *   k       lanes, 1..SB_MAX_LANES
  *   lane_k  HOST array of k+1 int32 offsets of the reduction dimension:

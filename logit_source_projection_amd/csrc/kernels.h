@@ -202,6 +202,20 @@ hipError_t launch_reconstruct(const LaneTable &lanes, int32_t B, float *logits,
 hipError_t launch_row_argmax(const float *logits, int64_t ldl, int32_t B, int32_t V,
                              int2 *partial, int32_t *ids, hipStream_t s);
 
+// Launch limits.  A HIP launch holds fewer than 2^32 work items in each grid
+// dimension and at most kMaxGridRows workgroups in y and z.  The launches with
+// one row per y index (normalize, reconstruct, row argmax, partial reduce) run
+// over longer batches in slices of kMaxGridRows rows; every other launch must
+// fit in one grid, which validation checks with the functions below.
+constexpr int kMaxGridRows = 65535;
+// Work items of the largest x dimension of any launch a head call on B rows
+// with these lane offsets makes, counted for the widest tile shifts, so that
+// the bound does not depend on where the shards sit.
+int64_t head_launch_items(int32_t B, int32_t H, int32_t V, const int32_t *lane_off, int32_t k);
+// The same for a partial-completion call of B rows, N output columns and
+// `chunks` reduction chunks.
+int64_t partial_launch_items(int32_t B, int32_t N, int32_t chunks);
+
 // ---------------------------------------------------------------------------
 // Partial completion: lane i holds an activation shard X_i [B][K_i] and the
 // matching weight rows W_i [K_i][N]; its partial is P_i = X_i . W_i, and a

@@ -35,6 +35,7 @@
 #include "kernels.h"
 
 #include <atomic>
+#include <algorithm>
 
 #include <float.h>
 #include <limits.h>
@@ -1205,6 +1206,18 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
     }
 }
 
+// Workgroups of a large-batch launch over mblocks x nblocks blocks: in the
+// super-tile order, whole super tiles, and a multiple of 8 of them.
+int64_t large_workgroups(int mblocks, int64_t nblocks)
+{
+    const int sm = super_rows(mblocks);
+    if (sm == 0)
+        return (int64_t)mblocks * nblocks;
+    const int sn = kSuperWG / sm;
+    const int64_t supers = (int64_t)((mblocks + sm - 1) / sm) * ((nblocks + sn - 1) / sn);
+    return (supers + 7) / 8 * 8 * kSuperWG;
+}
+
 template <int EPI, int BM, int BK, int ST>
 hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
 {
@@ -1213,16 +1226,8 @@ hipError_t launch_large_epi(const HeadArgs &a, hipStream_t s)
     g.nblocks = 0;
     for (int i = 0; i < a.lanes.k; ++i)
         g.nblocks += (a.lanes.off[i + 1] - a.lanes.off[i] + a.lanes.shift[i] + kLBN - 1) / kLBN;
-    int64_t nwg;
     g.sm = super_rows(g.mblocks);
-    if (g.sm > 0) {
-        const int sn = kSuperWG / g.sm;
-        const int64_t supers =
-            (int64_t)((g.mblocks + g.sm - 1) / g.sm) * ((g.nblocks + sn - 1) / sn);
-        nwg = ((supers + 7) / 8) * 8 * kSuperWG;
-    } else {
-        nwg = (int64_t)g.mblocks * g.nblocks;
-    }
+    const int64_t nwg = large_workgroups(g.mblocks, g.nblocks);
     const size_t lds = (size_t)LargeShape<BM, BK, ST>::kLdsBytes;
     static std::atomic<uint64_t> lds_done{0};
     const hipError_t e =
@@ -1551,9 +1556,15 @@ hipError_t launch_normalize(float *lp, int64_t ld, const float *lse, int32_t B, 
     const hipError_t e = raise_lds_limit((const void *)normalize_kernel, kNormLdsBytes, lds_done);
     if (e != hipSuccess)
         return e;
-    dim3 grid((V + kNormCols - 1) / kNormCols, B);
-    hipLaunchKernelGGL(normalize_kernel, grid, dim3(kThreads), kNormLdsBytes, s, lp, ld, lse, V);
-    return hipGetLastError();
+    for (int32_t r0 = 0; r0 < B; r0 += kMaxGridRows) {
+        const dim3 grid((V + kNormCols - 1) / kNormCols, min(B - r0, kMaxGridRows));
+        hipLaunchKernelGGL(normalize_kernel, grid, dim3(kThreads), kNormLdsBytes, s,
+                           lp + (int64_t)r0 * ld, ld, lse + r0, V);
+        const hipError_t el = hipGetLastError();
+        if (el != hipSuccess)
+            return el;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_reconstruct(const LaneTable &lanes, int32_t B, float *logits, int64_t ldl,
@@ -1564,9 +1575,19 @@ hipError_t launch_reconstruct(const LaneTable &lanes, int32_t B, float *logits, 
     int maxv = 0;
     for (int i = 0; i < lanes.k; ++i)
         maxv = max(maxv, lanes.off[i + 1] - lanes.off[i]);
-    dim3 grid((maxv + 4 * kThreads - 1) / (4 * kThreads), B, lanes.k);
-    hipLaunchKernelGGL(reconstruct_kernel, grid, dim3(kThreads), 0, s, lanes, logits, ldl);
-    return hipGetLastError();
+    LaneTable part = lanes;
+    for (int32_t r0 = 0; r0 < B; r0 += kMaxGridRows) {
+        for (int i = 0; i < lanes.k; ++i)
+            part.shard[i] = lanes.shard[i] + (int64_t)r0 * lanes.shard_ld[i];
+        const dim3 grid((maxv + 4 * kThreads - 1) / (4 * kThreads), min(B - r0, kMaxGridRows),
+                        lanes.k);
+        hipLaunchKernelGGL(reconstruct_kernel, grid, dim3(kThreads), 0, s, part,
+                           logits + (int64_t)r0 * ldl, ldl);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_row_argmax(const float *logits, int64_t ldl, int32_t B, int32_t V,
@@ -1575,11 +1596,14 @@ hipError_t launch_row_argmax(const float *logits, int64_t ldl, int32_t B, int32_
     if (B <= 0)
         return hipSuccess;
     const int nchunks = (V + kArgmaxChunk - 1) / kArgmaxChunk;
-    hipLaunchKernelGGL(row_argmax_kernel, dim3(nchunks, B), dim3(kThreads), 0, s, logits, ldl, V,
-                       nchunks, partial);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
+    for (int32_t r0 = 0; r0 < B; r0 += kMaxGridRows) {
+        hipLaunchKernelGGL(row_argmax_kernel, dim3(nchunks, min(B - r0, kMaxGridRows)),
+                           dim3(kThreads), 0, s, logits + (int64_t)r0 * ldl, ldl, V, nchunks,
+                           partial + (int64_t)r0 * nchunks);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     LaneTable one = {};
     one.k = 1;
     one.off[0] = 0;
@@ -1618,12 +1642,53 @@ hipError_t launch_partial_reduce(const PartialArgs &a, int op, float *out, int64
         constexpr int cols = kThreads / 8 * 4;
         hipLaunchKernelGGL(partial_reduce_kernel<8>, dim3((a.N + cols - 1) / cols, a.B),
                            dim3(kThreads), 0, s, a, op, out, ldo);
-    } else {
-        constexpr int cols = kThreads / 4 * 4;
-        hipLaunchKernelGGL(partial_reduce_kernel<4>, dim3((a.N + cols - 1) / cols, a.B),
-                           dim3(kThreads), 0, s, a, op, out, ldo);
+        return hipGetLastError();
     }
-    return hipGetLastError();
+    // Slices of kMaxGridRows rows: the kernel finds row b of chunk c at
+    // part + (c * a.B + b) * ldp, so moving part and out by r0 rows (a.B
+    // unchanged) makes y index b stand for row r0 + b.
+    constexpr int cols = kThreads / 4 * 4;
+    PartialArgs slice = a;
+    for (int32_t r0 = 0; r0 < a.B; r0 += kMaxGridRows) {
+        slice.part = a.part + (int64_t)r0 * a.ldp;
+        hipLaunchKernelGGL(partial_reduce_kernel<4>,
+                           dim3((a.N + cols - 1) / cols, min(a.B - r0, kMaxGridRows)),
+                           dim3(kThreads), 0, s, slice, op, out + (int64_t)r0 * ldo, ldo);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+int64_t head_launch_items(int32_t B, int32_t H, int32_t V, const int32_t *lane_off, int32_t k)
+{
+    if (B <= 0)
+        return 0;
+    int64_t tiles = 0, nblocks = 0;
+    for (int i = 0; i < k; ++i) {
+        const int64_t vi = (int64_t)lane_off[i + 1] - lane_off[i];
+        tiles += (vi + kMaxShift + kTileN - 1) / kTileN;
+        nblocks += (vi + kMaxShift + kLBN - 1) / kLBN;
+    }
+    // the combine launches: one workgroup per row
+    int64_t items = (int64_t)B * kThreads;
+    if (B >= kLargeBatch) {
+        const int mblocks = (B + large_block_rows(B) - 1) / large_block_rows(B);
+        items = std::max<int64_t>(items, large_workgroups(mblocks, nblocks) * kLThreads);
+    } else {
+        items = std::max<int64_t>(items, (tiles + 7) / 8 * 8 * k_slices(B, H, V) * kThreads);
+    }
+    return items;
+}
+
+int64_t partial_launch_items(int32_t B, int32_t N, int32_t chunks)
+{
+    if (B <= 0)
+        return 0;
+    const int64_t T = (N + kTileN - 1) / kTileN;
+    const int64_t groups = (B + rows_per_group(B) - 1) / rows_per_group(B);
+    return (int64_t)chunks * T * groups * kThreads;
 }
 
 // ---------------------------------------------------------------------------

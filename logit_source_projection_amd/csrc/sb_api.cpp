@@ -13,8 +13,10 @@
 
 namespace {
 
-constexpr int64_t kMaxRows = 65535;
 constexpr size_t kRegionAlign = 256;
+// Column counts and grid sizes over the vocabulary are 32-bit with room for
+// a chunk's rounding.
+constexpr int32_t kMaxVocab = 1 << 30;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -62,7 +64,7 @@ sb_status check_desc(const sb_head_desc *d)
             if (!aligned16(d->w[i]))
                 return SB_ERR_ALIGN;
     }
-    if (d->B > kMaxRows)
+    if (d->V > kMaxVocab)
         return SB_ERR_UNSUPPORTED;
     // Per-step buffer offsets are 32-bit: 40 hidden rows of a shard and one
     // row group of x must span less than 4 GiB; for the large-batch kernel
@@ -75,6 +77,10 @@ sb_status check_desc(const sb_head_desc *d)
     if (d->B >= sbk::kLargeBatch &&
         ((int64_t)(sbk::large_step_k(d->B) + 8) * d->ldw * 2 >= lim ||
          (int64_t)sbk::large_block_rows(d->B) * d->ldx * 2 >= lim))
+        return SB_ERR_UNSUPPORTED;
+    // every launch fits one grid (fewer than 2^32 work items per dimension);
+    // among others this bounds B below 2^24, the combine's one workgroup per row
+    if (sbk::head_launch_items(d->B, d->H, d->V, d->lane_off, d->k) >= lim)
         return SB_ERR_UNSUPPORTED;
     return SB_OK;
 }
@@ -294,12 +300,18 @@ sb_status check_partial(const sb_partial_desc *d)
             if (!aligned16(d->x[i]) || !aligned16(d->w[i]))
                 return SB_ERR_ALIGN;
     }
-    if (d->B > kMaxRows)
-        return SB_ERR_UNSUPPORTED;
     // per-chunk buffer offsets are 32-bit: a chunk of weight rows and one row
     // group of an activation shard must span less than 4 GiB
-    if ((int64_t)(sbk::kPartChunk + 8) * d->ldw * 2 >= ((int64_t)1 << 32) ||
-        (int64_t)(sbk::kRowBlock * sbk::kMaxMB) * d->ldx * 2 >= ((int64_t)1 << 32))
+    const int64_t lim = (int64_t)1 << 32;
+    if ((int64_t)(sbk::kPartChunk + 8) * d->ldw * 2 >= lim ||
+        (int64_t)(sbk::kRowBlock * sbk::kMaxMB) * d->ldx * 2 >= lim)
+        return SB_ERR_UNSUPPORTED;
+    // the chunked GEMM's launch fits one grid
+    int64_t chunks = 0;
+    for (int i = 0; i < d->k; ++i)
+        chunks += ((int64_t)d->lane_k[i + 1] - d->lane_k[i] + sbk::kPartChunk - 1) /
+                  sbk::kPartChunk;
+    if (sbk::partial_launch_items(d->B, d->N, (int32_t)chunks) >= lim)
         return SB_ERR_UNSUPPORTED;
     return SB_OK;
 }

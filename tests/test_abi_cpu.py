@@ -166,8 +166,7 @@ def test_workspace_bytes_of_a_split_head():
     (dict(w_ptrs=[FAKE, FAKE + 2 * 2047]), sb.SB_ERR_ALIGN),
     (dict(x_ptr=0), sb.SB_ERR_NULL),
     (dict(w_ptrs=[FAKE, 0]), sb.SB_ERR_NULL),
-    (dict(B=70000), sb.SB_ERR_UNSUPPORTED),
-    (dict(B=65536), sb.SB_ERR_UNSUPPORTED),
+    (dict(B=1 << 24), sb.SB_ERR_UNSUPPORTED),  # the combine's grid: 2^32 work items
     (dict(ldx=1 << 25), sb.SB_ERR_UNSUPPORTED),  # 64 rows of x span 4 GiB
     (dict(V=(1 << 31) - 8, off=(0, (1 << 31) - 8), ldw=(1 << 31) - 8), sb.SB_ERR_UNSUPPORTED),
 ])
@@ -207,6 +206,66 @@ def test_large_batch_offset_limits():
     assert tokens_status(fake_head(B=129, ldx=ldx256)) == sb.SB_ERR_UNSUPPORTED
     assert tokens_status(fake_head(B=100, ldx=ldx128)) == sb.SB_ERR_UNSUPPORTED
     assert tokens_status(fake_head(B=300, ldw=ldw)) == sb.SB_ERR_UNSUPPORTED
+
+
+def test_launch_size_limits():
+    """Every launch of a call fits one grid: fewer than 2^32 work items in its
+    x dimension.  The launches with one row per y index run over batches of
+    more than 65535 rows in slices, so B is not bounded by the y dimension."""
+    lim = 1 << 32
+    # (accepted descriptors are only sized, never run: their pointers are fake)
+    for B in (65535, 65536, 70000, 1 << 20):
+        assert ws_status(fake_head(B=B)) == sb.SB_OK, B
+    # the combine: one 256-item workgroup per row
+    assert (1 << 24) * 256 >= lim and ((1 << 24) - 1) * 256 < lim
+    assert ws_status(fake_head(B=(1 << 24) - 1)) == sb.SB_OK
+    assert ws_status(fake_head(B=1 << 24)) == sb.SB_ERR_UNSUPPORTED
+    # the large-batch kernel: 512-item workgroups over 256-row m-blocks and
+    # 256-column n-blocks, here 4096 m-blocks in super tiles of 8 x 4 blocks
+    # (32 workgroups), a multiple of 8 super tiles; an n-block count includes
+    # up to 56 columns of tile shift
+    def items(nblocks):
+        supers = 4096 // 8 * -(-nblocks // 4)
+        return -(-supers // 8) * 8 * 32 * 512
+
+    B = 1 << 20
+    big = fake_head(B=B, V=1 << 20, off=(0, 1 << 20))
+    small = fake_head(B=B, V=1 << 18, off=(0, 1 << 18))
+    assert items(4097) >= lim > items(1025)
+    assert ws_status(big) == sb.SB_ERR_UNSUPPORTED
+    assert tokens_status(big) == sb.SB_ERR_UNSUPPORTED
+    assert ws_status(small) == sb.SB_OK
+
+
+def test_vocabulary_limit():
+    """V <= 2^30 (32-bit column arithmetic with room for rounding), here over
+    64 lanes so that no shard's 72-row step reaches 4 GiB; the decode
+    kernel's one 256-item workgroup per 128-column tile then stays below
+    2^32 work items."""
+    for V, status in ((1 << 30, sb.SB_OK), ((1 << 30) + 8, sb.SB_ERR_UNSUPPORTED)):
+        off = [V * i // 64 // 8 * 8 for i in range(64)] + [V]
+        wide = max(off[i + 1] - off[i] for i in range(64))
+        assert 72 * wide * 2 < 1 << 32 and (V // 128 + 64 + 8) * 256 < 1 << 32
+        for B in (1, 64, 65, 200):
+            h = fake_head(B=B, V=V, off=off, ldw=(wide + 7) // 8 * 8, w_ptrs=[FAKE] * 64)
+            assert ws_status(h) == status, (V, B)
+
+
+def test_partial_launch_size_limits():
+    """The chunked partial GEMM runs ceil(B / 64) row groups (from 33 rows)
+    for every chunk and 128-column tile in one grid of 256-item workgroups:
+    18 chunks x 40 tiles here."""
+    lim = 1 << 32
+    ok_rows = (lim - 1) // (18 * 40 * 256) * 64
+    assert 18 * 40 * (ok_rows // 64) * 256 < lim <= 18 * 40 * (ok_rows // 64 + 1) * 256
+    for B, status in ((70000, sb.SB_OK), (ok_rows, sb.SB_OK),
+                      (ok_rows + 1, sb.SB_ERR_UNSUPPORTED)):
+        p = fake_partial(B=B)
+        st = ctypes.c_int(123)
+        sb.lib().sb_partial_workspace_bytes(p.ref(), ctypes.byref(st))
+        assert st.value == status, B
+    # (only the refused descriptor is passed to the call: the pointers are fake)
+    assert partial_status(fake_partial(B=ok_rows + 1), ws_bytes=1 << 62) == sb.SB_ERR_UNSUPPORTED
 
 
 def test_lane_results_checks():
@@ -328,7 +387,7 @@ def test_partial_workspace_bytes():
     (dict(w_ptrs=[FAKE + 2, FAKE]), sb.SB_ERR_ALIGN),
     (dict(x_ptrs=[FAKE, 0]), sb.SB_ERR_NULL),
     (dict(w_ptrs=[0, FAKE]), sb.SB_ERR_NULL),
-    (dict(B=65536), sb.SB_ERR_UNSUPPORTED),
+    (dict(B=1 << 24), sb.SB_ERR_UNSUPPORTED),  # the chunked GEMM's grid
     (dict(ldw=1 << 21), sb.SB_ERR_UNSUPPORTED),  # a 1024-row chunk spans 4 GiB
 ])
 def test_partial_descriptor_validation(kw, status):

@@ -132,10 +132,15 @@ def test_degenerate_heads(require_gpu, B, H, V, off):
     _case(d, lanes_separate=True, pad_x=(8 - H % 8) % 8)
 
 
-def test_maximum_batch(require_gpu):
-    """B = 65535 (the ABI's maximum): 256 row blocks of the large-batch kernel."""
-    d = inputs.make_random(65535, 40, 520, [0, 256, 520], seed=3000)
-    _case(d, full_logprobs=False)
+@pytest.mark.parametrize("B", [65535, 70000])
+def test_batches_up_to_and_past_one_launch_of_rows(require_gpu, B):
+    """A launch has at most 65535 workgroups in y: the launches with one row
+    per y index (normalize, reconstruct, the full-logit argmax) run over
+    70000 rows as two slices (65535 rows, then 4465).  Every surface,
+    complete log-probs included, against the oracle on every row; 256 and
+    274 row blocks of the large-batch kernel."""
+    d = inputs.make_random(B, 40, 520, [0, 256, 520], seed=3000 + B % 7)
+    _case(d)
 
 
 def test_empty_hidden_size(require_gpu):

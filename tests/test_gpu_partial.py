@@ -74,6 +74,7 @@ CASES = [
     (300, (700, 700), 200),
     (3, (1, 9), 1),       # one output column, a one-row shard
     (2, (31,), 8),
+    (70000, (300, 200), 40),  # the lane reduction over two 65535-row launches
 ]
 
 
