@@ -17,6 +17,8 @@ FLAGS = [
     # every symbol resolved at link time: a kernel template that failed to
     # instantiate is an error here, not a library that fails to load
     "-Wl,-z,defs",
+    # export the sb_* calls of include/sb.h and nothing else
+    "-Wl,--version-script=" + os.path.join(CSRC, "libsb.map"),
 ]
 
 
