@@ -34,8 +34,15 @@
  *    the complete log-probs) can differ in the last bits between shard
  *    placements that differ modulo 128 bytes; for the same placement it is
  *    reproduced exactly.
- *  - Inputs must be finite with |logit| < FLT_MAX; behaviour on NaN/Inf input
- *    is unspecified.
+ *  - Non-finite values: the argmax puts a NaN above every number (all NaNs
+ *    equal, so the lowest-index NaN wins, as numpy's and torch's argmax do)
+ *    and +inf above every finite value, so every ID, and every lane's ID, is
+ *    one of the row's columns whatever the inputs.  NaN and infinities in x
+ *    or w reach the fp32 logits by IEEE rules (NaN * anything and 0 * inf
+ *    give NaN).  lse, sel_lp and the complete log-probs of a row holding a
+ *    NaN or +inf logit are NaN; of a row of -inf only, unspecified.  Finite
+ *    inputs whose sums overflow fp32 are outside the contract
+ *    (|logit| < FLT_MAX).
  *
  * Ownership and threading
  *  - The caller allocates every device buffer.  The library allocates no

@@ -94,9 +94,43 @@ static hipError_t raise_lds_limit(const void *kernel, int bytes, std::atomic<uin
     return e;
 }
 
+// The order of the argmax over (value, index): NaN above every number (the
+// convention of numpy's and torch's argmax), then the order of the floats
+// (+inf above every finite value, -0 equal to +0), and between equal values
+// -- all NaNs count as equal -- the lower index.  It is a total order, so
+// the result does not depend on the order of the fold, and every row's ID is
+// one of its columns whatever its values.
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2)
 {
+    const bool n1 = v1 != v1, n2 = v2 != v2;
+    if (n1 || n2)
+        return n1 && (!n2 || i1 < i2);
     return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// better() for a candidate whose index is higher than the current best's.
+__device__ __forceinline__ bool above(float v, float best)
+{
+    return v > best || (v != v && best == best);
+}
+
+// The same order on values known to hold no NaN: one compare.  The head
+// epilogues use it unless a wave finds a NaN among its values (any_nan8).
+__device__ __forceinline__ bool better_num(float v1, int i1, float v2, int i2)
+{
+    return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// Whether any of eight values is NaN: a NaN-propagating maximum of all of
+// them (v_maximum3_f32, four instructions) compared with itself.
+__device__ __forceinline__ bool any_nan8(float a, float b, float c, float d, float e, float f,
+                                         float g, float h)
+{
+    const float m = __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c),
+        __builtin_elementwise_maximum(__builtin_elementwise_maximum(d, e),
+                                      __builtin_elementwise_maximum(__builtin_elementwise_maximum(f, g), h)));
+    return m != m;
 }
 
 // Online logsumexp merge of (m2, s2) into (m1, s1); -inf marks "empty".
@@ -141,24 +175,62 @@ __device__ __forceinline__ float dpp_float(float v)
     return __int_as_float(dpp_int<CTRL>(__float_as_int(v)));
 }
 
-template <int CTRL>
+template <int CTRL, bool NAN_AWARE>
 __device__ __forceinline__ void best_step(float &bv, int &bi)
 {
     const float ov = dpp_float<CTRL>(bv);
     const int oi = dpp_int<CTRL>(bi);
-    if (better(ov, oi, bv, bi)) {
+    if (NAN_AWARE ? better(ov, oi, bv, bi) : better_num(ov, oi, bv, bi)) {
         bv = ov;
         bi = oi;
     }
 }
 
 // (max, lowest index) over each 16-lane row; every lane gets its row's.
+// NAN_AWARE = false only where the wave holds no NaN.
+template <bool NAN_AWARE = true>
 __device__ __forceinline__ void row16_best(float &bv, int &bi)
 {
-    best_step<kDppQuadXor1>(bv, bi);
-    best_step<kDppQuadXor2>(bv, bi);
-    best_step<kDppHalfMirror>(bv, bi);
-    best_step<kDppMirror>(bv, bi);
+    best_step<kDppQuadXor1, NAN_AWARE>(bv, bi);
+    best_step<kDppQuadXor2, NAN_AWARE>(bv, bi);
+    best_step<kDppHalfMirror, NAN_AWARE>(bv, bi);
+    best_step<kDppMirror, NAN_AWARE>(bv, bi);
+}
+
+// The (max, lowest index) of each 16-lane row of a head epilogue, over the
+// eight values y0..y7 of each thread at global columns gcol.. (the first
+// nvalid of them real columns): the plain comparison, or, when any value
+// of the wave is NaN, the NaN-aware order.  The branch is uniform over the
+// wave, so the DPP steps see every lane of their rows.
+__device__ __forceinline__ void tile_best(float y0, float y1, float y2, float y3, float y4,
+                                          float y5, float y6, float y7, int nvalid, int gcol,
+                                          float &bv, int &bi)
+{
+    const float y[8] = {y0, y1, y2, y3, y4, y5, y6, y7};
+    bv = -INFINITY;
+    bi = INT_MAX;
+    if (nvalid > 0) {
+        bv = y[0];
+        bi = gcol;
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(any_nan8(y0, y1, y2, y3, y4, y5, y6, y7)) == 0,
+                         1)) {
+#pragma unroll
+        for (int j = 1; j < 8; ++j)
+            if (j < nvalid && y[j] > bv) {
+                bv = y[j];
+                bi = gcol + j;
+            }
+        row16_best<false>(bv, bi);
+    } else {
+#pragma unroll
+        for (int j = 1; j < 8; ++j)
+            if (j < nvalid && above(y[j], bv)) {
+                bv = y[j];
+                bi = gcol + j;
+            }
+        row16_best<true>(bv, bi);
+    }
 }
 
 // Sum over each 16-lane row; every lane gets its row's.
@@ -340,21 +412,11 @@ __device__ __forceinline__ void emit_tile_row(const HeadArgs &a, const float (&y
         }
     }
     if (EPI != kEpiShard) {
-        // (max, lowest index) over the thread's columns, ascending.
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-        if (nvalid > 0) {
-            bv = y[0];
-            bi = gcol;
-        }
-#pragma unroll
-        for (int j = 1; j < 8; ++j)
-            if (j < nvalid && y[j] > bv) {
-                bv = y[j];
-                bi = gcol + j;
-            }
+        // (max, lowest index) over the thread's columns, ascending, then
         // across the 16 threads of this row (one 16-lane row of the wave)
-        row16_best(bv, bi);
+        float bv;
+        int bi;
+        tile_best(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7], nvalid, gcol, bv, bi);
         float se = 0.f;
         if (EPI != kEpiPair) {
 #pragma unroll
@@ -1174,19 +1236,9 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
                 }
             }
             if (EPI != kEpiShard) {
-                float bv = -INFINITY;
-                int bi = INT_MAX;
-                if (nvalid > 0) {
-                    bv = y[0];
-                    bi = gcol;
-                }
-#pragma unroll
-                for (int c = 1; c < 8; ++c)
-                    if (c < nvalid && y[c] > bv) {
-                        bv = y[c];
-                        bi = gcol + c;
-                    }
-                row16_best(bv, bi);
+                float bv;
+                int bi;
+                tile_best(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7], nvalid, gcol, bv, bi);
                 float se = 0.f;
                 if (EPI != kEpiPair) {
 #pragma unroll

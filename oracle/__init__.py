@@ -28,6 +28,10 @@ Readings taken where the pages are silent:
 * log-probabilities are log-softmax of the raw logits (no temperature, bias or
   soft-cap); the selected-token log-probability belongs to the argmax token;
 * the argmax is decided on the fp64 logits themselves (the plain definition);
+* non-finite logits follow numpy's argmax: a NaN ranks above every number
+  (the first NaN wins), +inf above every finite value, so every row has an
+  ID among its columns; the log-prob values of a row holding a NaN or +inf
+  are not defined by the pages (NaN falls out of the formulas here);
 * a row is a "near tie" when its fp64 top-2 gap (largest logit minus the
   next largest, over distinct indices) is below 2e-3 * max_v |z|.
 
@@ -158,14 +162,19 @@ def combine(M, A, S):
     """Fold the per-lane results in ascending lane order (one int32 result per
     lane is what source projection ships, SemBridge section 6).
 
-      id  = A_j for the first lane j whose M_j equals m = max_i M_i
+      id  = A_j for the first lane j whose M_j is the largest, m = M_j
       lse = m + log(sum_i S_i * exp(M_i - m))
+    "Largest" is np.argmax's order, the same as the per-lane argmax: a NaN
+    ranks above every number (the first NaN wins), so the fold picks the lane
+    of the row's first NaN when there is one; with finite values it is the
+    first lane attaining max_i M_i.
     Returns (ids int64 [B], lse float64 [B]).
     """
     B, k = M.shape
-    m = M.max(axis=1)
-    j = np.argmax(M == m[:, None], axis=1)  # first lane holding the max
-    ids = A[np.arange(B), j]
+    rows = np.arange(B)
+    j = np.argmax(M, axis=1)  # first lane holding the largest result
+    m = M[rows, j]
+    ids = A[rows, j]
     lse = m + np.log((S * np.exp(M - m[:, None])).sum(axis=1))
     return ids, lse
 
