@@ -964,6 +964,30 @@ __device__ __forceinline__ int x_swz(int r, int j)
     return P == 4 ? ((r >> 2) & 3) : (((r >> 1) & 3) | ((j & 1) << 2));
 }
 
+// Zero the hidden positions at and past `hrem` (0 < hrem < BK) of an X stage
+// of BM rows in LDS.  The last stage of a head whose H is not a multiple of
+// BK holds the row padding of X there, which may be any bits (NaN included);
+// the weight rows past H arrive as zeros (they lie past the weight buffer's
+// extent), so after this every product past H is an exact +0 and the hot
+// loop needs no masking.  Only that last stage calls it, after its loads
+// have landed and before any wave reads it.
+template <int BM, int P>
+__device__ __forceinline__ void large_zero_x_tail(uint8_t *xst, int hrem)
+{
+    constexpr int R = 64 / P;
+    for (int idx = threadIdx.x; idx < BM * P; idx += kLThreads) {
+        const int row = idx / P, q = idx % P;
+        const int e0 = 8 * q;  // the piece's first hidden position in the stage
+        if (e0 + 8 <= hrem)
+            continue;
+        const int j = row / R, r = row % R;
+        uint16_t *piece =
+            reinterpret_cast<uint16_t *>(xst + j * 1024 + (r * P + (q ^ x_swz<P>(r, j))) * 16);
+        for (int e = max(hrem - e0, 0); e < 8; ++e)
+            piece[e] = 0;
+    }
+}
+
 struct LargeGrid {
     int mblocks;  // ceil(B / block rows)
     int sm;       // m-blocks per super-tile (8, 4 or 2), or 0 for the plain order
@@ -1146,50 +1170,47 @@ __global__ __launch_bounds__(kLThreads, 1) void head_gemm_large_kernel(const Hea
             large_stage_loads<kXInst, kWInst, BK>(xring + slot * kStageXBytes, wring + slot * kStageWBytes,
                                       xbase, xbytes, wbase, wbytes, sn, a.ldw, xvo, wvo, wave);
         }
+        if (st * BK + BK > H) {
+            // the last stage of a ragged H: zero X past H, then let every wave see it
+            large_zero_x_tail<BM, kPieces>(xring + (st % kStages) * kStageXBytes, H - st * BK);
+            __syncthreads();
+        }
         const uint8_t *stage = xring + (st % kStages) * kStageXBytes;
         const uint8_t *wst = wring + (st % kStages) * kStageWBytes;
+        // every fragment of the stage first (both 32-deep steps of a 64-deep
+        // stage), so that the second step's reads overlap the first step's MFMAs
+        u32x4 af[kSub][RB], wq[kSub][8];
 #pragma unroll
         for (int ks = 0; ks < kSub; ++ks) {
-            const int k0 = st * BK + 32 * ks;
-            u32x4 af[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const int row = wr * kWaveRows + rb * 16 + n;
                 const int j = row / kRowsPerInst, r = row % kRowsPerInst;
                 const int piece = 4 * ks + g;
-                af[rb] = *reinterpret_cast<const u32x4 *>(
+                af[ks][rb] = *reinterpret_cast<const u32x4 *>(
                     stage + j * 1024 + (r * kPieces + (piece ^ x_swz<kPieces>(r, j))) * 16);
             }
-            if (k0 + 32 > H) {
-                const int h0 = k0 + 8 * g;
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        uint32_t v = af[rb][d];
-                        if (h0 + 2 * d >= H)
-                            v &= 0xFFFF0000u;
-                        if (h0 + 2 * d + 1 >= H)
-                            v &= 0x0000FFFFu;
-                        af[rb][d] = v;
-                    }
-            }
-            u32x4 wq[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r)
-                wq[r] = *reinterpret_cast<const u32x4 *>(wst + (32 * ks + 8 * g + r) * (kLBN * 2) +
-                                                         (wc * 128 + 8 * n) * 2);
+                wq[ks][r] = *reinterpret_cast<const u32x4 *>(
+                    wst + (32 * ks + 8 * g + r) * (kLBN * 2) + (wc * 128 + 8 * n) * 2);
+        }
+        // keep the reads ahead of the MFMAs (the scheduler would sink them)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < kSub; ++ks) {
             bf16x8 xa[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                xa[rb] = __builtin_bit_cast(bf16x8, af[rb]);
+                xa[rb] = __builtin_bit_cast(bf16x8, af[ks][rb]);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
                 u32x4 bq;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    bq[q] = __builtin_amdgcn_perm(wq[2 * q + 1][c >> 1], wq[2 * q][c >> 1], sel);
+                    bq[q] = __builtin_amdgcn_perm(wq[ks][2 * q + 1][c >> 1], wq[ks][2 * q][c >> 1],
+                                                  sel);
                 const bf16x8 bb = __builtin_bit_cast(bf16x8, bq);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
