@@ -248,7 +248,9 @@ sb_status sb_full_logits(const sb_head_desc *desc, float *logits, int64_t ldl,
  * is exposed:  out = op(...op(op(P_0, P_1), P_2)..., P_{k-1})  (ascending
  * lane order).  Each P_i is accumulated in an order fixed by the shapes
  * alone (1024-row chunks summed in a fixed order), so repeated calls give
- * bit-identical outputs.
+ * bit-identical outputs.  SB_RED_MIN and SB_RED_MAX propagate NaN (IEEE
+ * 754-2019 minimum and maximum, as numpy's and torch's elementwise ones):
+ * an output is NaN when any lane's partial there is NaN.
  * ---------------------------------------------------------------------------
  */
 typedef enum sb_reduce_op {

@@ -1487,6 +1487,9 @@ __global__ __launch_bounds__(kThreads, Occupancy<MB>::kBlocksPerCU) void partial
     }
 }
 
+// The registered operator on two partials.  Minimum and maximum propagate
+// NaN (IEEE 754-2019 minimum / maximum: v_minimum_f32 / v_maximum_f32), as
+// numpy's and torch's do.
 __device__ __forceinline__ f32x4 reduce_op(int op, f32x4 a, f32x4 b)
 {
     switch (op) {
@@ -1495,9 +1498,9 @@ __device__ __forceinline__ f32x4 reduce_op(int op, f32x4 a, f32x4 b)
     case kRedProd:
         return a * b;
     case kRedMin:
-        return f32x4{fminf(a[0], b[0]), fminf(a[1], b[1]), fminf(a[2], b[2]), fminf(a[3], b[3])};
+        return __builtin_elementwise_minimum(a, b);
     default:
-        return f32x4{fmaxf(a[0], b[0]), fmaxf(a[1], b[1]), fmaxf(a[2], b[2]), fmaxf(a[3], b[3])};
+        return __builtin_elementwise_maximum(a, b);
     }
 }
 

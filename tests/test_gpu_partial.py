@@ -118,6 +118,24 @@ def test_repeated_calls_are_bitwise_identical(require_gpu):
         assert np.array_equal(a, run(part, op)), op
 
 
+@pytest.mark.parametrize("B", [3, 40, 100])
+def test_nan_partial_propagates(require_gpu, B):
+    """A NaN hidden value in one lane's shard makes that lane's partial NaN
+    across its row; every operator, minimum and maximum included, then gives
+    NaN across that row (as the oracle's np.minimum / np.maximum do), and
+    the other rows match the oracle as usual."""
+    xs, ws = inputs.draw_partial(B, 300, (700, 500, 90), seed=900 + B, sigma_w=0.05)
+    xs[1][B // 2, 17] = 0x7FC0
+    P = opart.partials(xs, ws)
+    part = upload(xs, ws)
+    others = np.array([b for b in range(B) if b != B // 2])
+    for op in opart.OPS:
+        g = run(part, op)
+        assert np.isnan(g[B // 2]).all(), op
+        assert not np.isnan(g[others]).any(), op
+        check(g[others], P[:, others], op)
+
+
 def test_empty_batch(require_gpu):
     xs, ws = inputs.draw_partial(1, 64, (64,), seed=8)
     part = upload(xs, ws)

@@ -121,6 +121,25 @@ def test_lane_order_does_not_change_min_max_and_moves_sum_only_in_last_bits():
     assert np.allclose(a["prod"], b["prod"], rtol=1e-14, atol=0)
 
 
+def test_nan_partial_propagates_through_every_operator():
+    """A NaN hidden value in lane 1's shard at row 2 makes that lane's
+    partial NaN across row 2 (IEEE: NaN times anything is NaN).  Sum and
+    product then give NaN there by IEEE arithmetic; minimum and maximum
+    by the reading taken for them (numpy's np.minimum / np.maximum, not
+    np.fmin / np.fmax, which would drop the NaN).  Every other row is
+    independent of row 2 and equals the completion without the NaN."""
+    xs, ws = tiny_lanes(4, (6, 7, 5), 9, 11)
+    xn = [x.copy() for x in xs]
+    xn[1][2, 3] = 0x7FC0                    # bf16 quiet NaN
+    rows = [0, 1, 3]
+    for op in partial.OPS:
+        clean = partial.partial_complete(xs, ws, op)
+        got = partial.partial_complete(xn, ws, op)
+        assert np.isnan(got[2]).all(), op
+        assert np.array_equal(got[rows], clean[rows]), op
+        assert not np.isnan(got[rows]).any(), op
+
+
 def test_rejects_bad_inputs():
     xs, ws = tiny_lanes(2, (4, 4), 3, 8)
     with pytest.raises(ValueError):
