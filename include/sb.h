@@ -51,7 +51,11 @@
  *    raised (hipFuncSetAttribute, once per device and kernel) and, for
  *    sb_project_tokens_static, each device's address of its static array.
  *  - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
- *    the default stream).  Inputs are read-only.
+ *    the default stream).  Inputs are read-only.  Every device pointer of a
+ *    call must be memory the stream's device can access (its own, or a
+ *    peer's with peer access enabled); the library does not check this, as
+ *    a per-call pointer query would cost more than a decode call's launch.
+ *    Outputs must not overlap inputs, the workspace or each other.
  *  - The workspace is scratch owned by the call until its work completes on
  *    the stream: its contents on entry do not matter, and nothing in it is
  *    valid afterwards.  Every workspace starts with the same fixed region
