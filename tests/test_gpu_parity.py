@@ -143,6 +143,18 @@ def test_batches_up_to_and_past_one_launch_of_rows(require_gpu, B):
     _case(d)
 
 
+@pytest.mark.parametrize("B", [3, 40, 70])
+def test_million_column_vocabulary(require_gpu, B):
+    """V = 1,048,583 (2^20 + 7) in three ragged lanes: about 8200 tiles per
+    row for the combine, the lse fold and the full-logit argmax (128 chunks),
+    through the decode kernel (3 rows; 40 rows with packed hidden rows) and
+    the large-batch kernel (70 rows, one 128-row block)."""
+    V = (1 << 20) + 7
+    off = [0, 300_001, 700_000, V]
+    d = inputs.make_random(B, 24, V, off, seed=4100 + B)
+    _case(d, lanes_separate=True)
+
+
 def test_empty_hidden_size(require_gpu):
     B, V = 3, 1000
     x = torch.empty((B, 0), dtype=torch.bfloat16, device="cuda")
