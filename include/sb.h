@@ -109,7 +109,10 @@ typedef enum sb_status {
                                 need 2^32 work items or more in one grid
                                 dimension (B >= 2^24 always does; for
                                 B >= 129 roughly B * V >= 5.5e11)          */
-    SB_ERR_HIP = -7          /* a HIP launch failed                            */
+    SB_ERR_HIP = -7,         /* a HIP launch failed                            */
+    /* not a status: widens the enumeration to every 32-bit int, so that
+       sb_status_string() may be given any value a caller holds */
+    SB_STATUS_RANGE_MAX_ = 0x7FFFFFFF
 } sb_status;
 
 #define SB_MAX_LANES 64
