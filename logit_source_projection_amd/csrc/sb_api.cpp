@@ -541,6 +541,8 @@ const char *sb_status_string(sb_status status)
         return "size beyond the supported limits";
     case SB_ERR_HIP:
         return "HIP launch failed";
+    case SB_STATUS_RANGE_MAX_:
+        break;
     }
     return "unknown status";
 }
